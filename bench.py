@@ -1,0 +1,237 @@
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+A step is one pass of the whole path (route -> permute -> grouped FFN ->
+combine) over one batch. Default workload: decode of two concurrent requests,
+T=2, H=2048, I=768, E=128, k=8, W4A16 g128, 48 independent layers per step
+(so one step is one decode step through a 48-layer MoE stack). All inputs are
+seeded synthetic tensors resident in HBM before the timed region.
+
+Prints one JSON line with the whole-job throughput (tokens/s), a roofline
+entry for the dominant kernel (the grouped FFN call: gate/up + down), and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK = {"bf16": 2500.0, "int8": 5000.0}   # dense, TFLOP/s (TOP/s for int8)
+METRIC = "MoE-FFN tokens/s; decode HBM GB/s % of peak; prefill MFMA % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_t2", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def stage(wl, torch):
+    """Upload every unit's inputs. Returns per-unit (x, logits, weights)."""
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).cuda()
+
+    units = []
+    wcache = {}
+    for u in range(wl.units):
+        wu = 0 if wl.shared_weights else u
+        if wu not in wcache:
+            arrs = synth.layer_w4(wl, wu) if wl.fmt == "w4a16" else synth.layer_w8(wl, wu)
+            wcache[wu] = tuple(dev(a) for a in arrs)
+            del arrs
+        units.append((dev(synth.x_bf16(wl, u)), dev(synth.router_logits(wl, u)), wcache[wu]))
+    torch.cuda.synchronize()
+    return units
+
+
+def expert_bytes(wl) -> int:
+    if wl.fmt == "w4a16":
+        return (2 * wl.I * wl.H // 2 + 2 * wl.I * (wl.H // 128) * 2
+                + wl.H * wl.I // 2 + wl.H * (wl.I // 128) * 2)
+    return 2 * wl.I * wl.H + 2 * wl.I * 4 + wl.H * wl.I + wl.H * 4
+
+
+def layers_per_step(wl) -> list:
+    """Units one step runs: every layer (decode/prefill stacks) or one unit."""
+    if wl.name in ("decode_t2", "prefill_t512"):
+        return [list(range(wl.units))]
+    return [[u] for u in range(wl.units)]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_moe_expert_top_amd as moe
+
+    torch.cuda.set_device(0)
+    moe.load()
+    wl = synth.workload(args.workload)
+    units = stage(wl, torch)
+    b = moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    shape = (wl.T, wl.H, wl.I, wl.E, wl.k)
+    ffn = moe.grouped_w4a16_ffn if wl.fmt == "w4a16" else moe.grouped_w8a8_ffn
+    schedule = layers_per_step(wl)
+    stream = torch.cuda.current_stream()
+
+    def layer(u, ev=None):
+        x, L, (w13, s13, w2, s2) = units[u]
+        moe.route_topk(L, wl.k, b.ids, b.w)
+        moe.permute(b.ids, wl.E, b.offsets, b.sorted_slot, b.slot_pos, b.active, b.n_active,
+                    b.perm_ws)
+        if ev is not None:
+            ev[0].record(stream)
+        ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active, b.n_active, b.y,
+            b.ffn_ws)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.combine(b.y, b.slot_pos, b.w, b.out)
+
+    def step(i, events=None):
+        for u in schedule[i % len(schedule)]:
+            ev = None
+            if events is not None:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                events.append((u, ev))
+            layer(u, ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, with HIP events around every grouped-FFN call
+    events = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+    value = wl.T * args.steps / (ms_total / 1e3)   # each step carries T tokens
+
+    # algorithmic bytes of each grouped-FFN call: routed experts' weights + x + y
+    act_per_unit = {}
+    for u in range(wl.units):
+        layer(u)
+        torch.cuda.synchronize()
+        act_per_unit[u] = int(b.n_active.cpu()[0])
+    eb = expert_bytes(wl)
+    io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 2
+    tot_bytes, tot_ms = 0.0, 0.0
+    for u, (e0, e1) in events:
+        tot_bytes += act_per_unit[u] * eb + io_bytes
+        tot_ms += e0.elapsed_time(e1)
+    n_calls = len(events)
+    avg_ms = tot_ms / n_calls
+    avg_bytes = tot_bytes / n_calls
+    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
+    flops_per_call = 2.0 * 3 * wl.H * wl.I * wl.T * wl.k
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "kernel": f"moe_grouped_{wl.fmt}_ffn (gate/up + down)",
+        "avg_launch_us": round(avg_ms * 1e3, 2),
+        "algo_bytes_per_launch": int(avg_bytes),
+    }
+    if wl.fmt == "w8a8" or wl.T >= 512:
+        dt = "int8" if wl.fmt == "w8a8" else "bf16"
+        roofline["mfma_frac"] = round(flops_per_call / (avg_ms / 1e3) / 1e12 / MFMA_PEAK[dt], 4)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, schedule, args.cpu_budget_s)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if wl.fmt == "w8a8" else "bf16",
+        "data": "synthetic (seeded; random int4/int8 expert weights, N(0,1) activations)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
+                   "format": "W4A16 g128" if wl.fmt == "w4a16" else "W8A8",
+                   "layers_per_step": len(schedule[0]),
+                   "mean_active_experts": round(float(np.mean(list(act_per_unit.values()))), 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, schedule, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    done = 0
+    el = 0.0
+    arrs = None
+    for u in range(wl.units):
+        # inputs are generated before the clock starts; only the oracle is timed
+        x, L = synth.x_bf16(wl, u), synth.router_logits(wl, u)
+        if arrs is None or not wl.shared_weights:
+            arrs = synth.layer_w4(wl, u) if wl.fmt == "w4a16" else synth.layer_w8(wl, u)
+        get = lambda e, a=arrs: tuple(t[e] for t in a)  # noqa: E731
+        t0 = time.perf_counter()
+        if wl.fmt == "w4a16":
+            oracle.moe_layer_w4a16(x, L, wl.k, get)
+        else:
+            oracle.moe_layer_w8a8(x, L, wl.k, get)
+        el += time.perf_counter() - t0
+        done += 1
+        if el > budget_s:
+            break
+    per_unit = el / done
+    per_step = per_unit * len(schedule[0])
+    return {
+        "value": round(wl.T / per_step, 4),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {wl.units} units of workload {wl.name} through the float64 numpy "
+                   f"oracle (input generation excluded); "
+                   f"{per_unit:.3f} s per unit, scaled to {len(schedule[0])} units per step"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,80 @@
+"""Routed MoE FFN over group-quantized experts on MI355X (gfx950).
+
+The layer runs as five calls into libmoe (HIP kernels behind a C ABI):
+route_topk -> permute -> grouped_w4a16_ffn | grouped_w8a8_ffn -> combine.
+PyTorch only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    MoeError, combine, grouped_w4a16_ffn, grouped_w8a8_ffn, load, permute,
+    permute_workspace, route_topk, w4a16_workspace, w8a8_workspace,
+)
+
+__all__ = ["MoeError", "LayerBuffers", "moe_forward", "load", "route_topk", "permute",
+           "grouped_w4a16_ffn", "grouped_w8a8_ffn", "combine"]
+
+
+@dataclass
+class LayerBuffers:
+    """Device buffers for one layer call (allocated once, reused across calls)."""
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    fmt: str
+    ids: object
+    w: object
+    offsets: object
+    sorted_slot: object
+    slot_pos: object
+    active: object
+    n_active: object
+    perm_ws: object
+    ffn_ws: object
+    y: object
+    out: object
+
+    @classmethod
+    def alloc(cls, T, H, I, E, k, fmt="w4a16", device="cuda"):
+        import torch
+        R = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        pws = _lib.permute_workspace(T, E, k)
+        fws = (_lib.w4a16_workspace if fmt == "w4a16" else _lib.w8a8_workspace)(T, H, I, E, k)
+        return cls(
+            T, H, I, E, k, fmt,
+            ids=torch.empty((T, k), **i32),
+            w=torch.empty((T, k), dtype=torch.float32, device=device),
+            offsets=torch.empty(E + 1, **i32),
+            sorted_slot=torch.empty(max(R, 1), **i32),
+            slot_pos=torch.empty(max(R, 1), **i32),
+            active=torch.empty(max(min(E, R), 1), **i32),
+            n_active=torch.empty(4, **i32),
+            perm_ws=torch.empty(max(pws, 16), dtype=torch.uint8, device=device),
+            ffn_ws=torch.empty(max(fws, 16), dtype=torch.uint8, device=device),
+            y=torch.empty((max(R, 1), H), dtype=torch.int16, device=device),
+            out=torch.empty((T, H), dtype=torch.float32, device=device),
+        )
+
+
+def moe_forward(b: LayerBuffers, x, logits, weights, debug=None, stream=None):
+    """One routed MoE FFN layer: x bf16 bits (int16 [T,H]), logits f32 [T,E],
+    weights = (w13, s13, w2, s2) in the layout of include/moe.h. Returns b.out."""
+    shape = (b.T, b.H, b.I, b.E, b.k)
+    _lib.route_topk(logits, b.k, b.ids, b.w, stream)
+    _lib.permute(b.ids, b.E, b.offsets, b.sorted_slot, b.slot_pos, b.active, b.n_active,
+                 b.perm_ws, stream)
+    w13, s13, w2, s2 = weights
+    if b.fmt == "w4a16":
+        _lib.grouped_w4a16_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
+                               b.n_active, b.y, b.ffn_ws, stream)
+    else:
+        _lib.grouped_w8a8_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
+                              b.n_active, b.y, b.ffn_ws, debug, stream)
+    _lib.combine(b.y, b.slot_pos, b.w, b.out, stream)
+    return b.out

@@ -1,0 +1,470 @@
+// Grouped SwiGLU expert FFN over W4A16 g128 weights.
+//
+// Weight format ("Measured results", header: W4A16 g128): 4-bit codes packed
+// two per byte along K (low nibble = even k), zero point 8, one fp16 scale per
+// (output row, 128-wide K group); W[n,k] = (q - 8) * s[n, k/128]. Weights are
+// used as stored ("Performance and verification", section "Why it is fast"):
+// codes are streamed once per call and widened in registers, never expanded
+// in memory (one layout serves decode and prefill: "Measured results",
+// section "Memory").
+//
+// Dequantization trick used by both kernels: a code q placed in the low
+// mantissa bits of bf16 0x4300 is exactly 128 + q. Dot products run on those
+// exact values; since the code is the same for the whole 128-wide group only
+// through its scale, the group's partial sum is
+//   sum_k x_k (q_k - 8) = sum_k x_k (128 + q_k) - 136 * sum_k x_k,
+// with the activation sums computed once when the activations are staged.
+// The scale is applied to the float32 partial sum of each group, so weights
+// are never rounded.
+//
+// Two kernels, chosen by batch size (a fixed rule, same tolerance for both):
+//  * decode (T <= 4): grouped GEMV. A block owns one routed expert and a strip
+//    of output rows; LK lanes split K with coalesced 16-byte code loads, the
+//    token rows live in LDS, and v_dot2_f32_bf16 does the products.
+//  * prefill: grouped GEMM on bf16 MFMA (v_mfma_f32_32x32x16_bf16). A block
+//    owns (expert, 32- or 64-row tile, column tile); codes go from HBM to
+//    registers and are widened right into the MFMA B operand; the gathered
+//    activation rows go through LDS.
+// Gate/up blocks pair gate row n with up row I + n in the same lane and apply
+// SwiGLU in the epilogue (h is stored bf16); down blocks write y (bf16).
+#include "common.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGemvMaxT = 4;
+
+// ---------------------------------------------------------------- GEMV ----
+// KIND 0: gate/up (A = x rows of the expert's tokens, out = h [R, I]).
+// KIND 1: down    (A = h rows of the expert's block,  out = y [R, N]).
+template <int KIND, int LK, int MAXM>
+__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
+    const uint16_t* __restrict__ S, const int* __restrict__ offsets,
+    const int* __restrict__ sorted_slot, const int* __restrict__ active,
+    const int* __restrict__ n_active, uint16_t* __restrict__ out, int K, int N, int topk,
+    int tiles) {
+  constexpr int G = kWave / LK;          // lane groups per wave
+  constexpr int UB = (kThreads / kWave) * G;  // units per block
+  const int a = blockIdx.x / tiles;
+  if (a >= *n_active) return;
+  const int tile = blockIdx.x - a * tiles;
+  const int e = active[a];
+  const int p0 = offsets[e];
+  const int M = offsets[e + 1] - p0;
+  const int C = K / 32;                  // 16-byte code chunks per row
+  const int units = (KIND == 0) ? N / 2 : N / 2;
+
+  extern __shared__ uint32_t lds[];
+  uint32_t* xs = lds;                                         // [MAXM][K/2]
+  float* csum = reinterpret_cast<float*>(lds + MAXM * (K / 2));  // [MAXM][C]
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  const int g = lane / LK, lk = lane % LK;
+  const int u = tile * UB + wv * G + g;
+  const bool valid = u < units;
+  const int uc = valid ? u : units - 1;
+  const int r0 = (KIND == 0) ? uc : 2 * uc;
+  const int r1 = (KIND == 0) ? N / 2 + uc : 2 * uc + 1;
+  const size_t rowb = static_cast<size_t>(K / 2), rows = static_cast<size_t>(K / kGroup);
+  const uint8_t* W0 = W + (static_cast<size_t>(e) * N + r0) * rowb;
+  const uint8_t* W1 = W + (static_cast<size_t>(e) * N + r1) * rowb;
+  const uint16_t* S0 = S + (static_cast<size_t>(e) * N + r0) * rows;
+  const uint16_t* S1 = S + (static_cast<size_t>(e) * N + r1) * rows;
+
+  for (int m0 = 0; m0 < M; m0 += MAXM) {
+    const int Mc = min(MAXM, M - m0);
+    // stage the rows: 32 values per (row, chunk), pair-permuted, plus sums
+    for (int i = tid; i < Mc * C; i += kThreads) {
+      const int m = i / C, c = i - m * C;
+      const int p = p0 + m0 + m;
+      const uint16_t* src = (KIND == 0)
+          ? A + static_cast<size_t>(sorted_slot[p] / topk) * K + c * 32
+          : A + static_cast<size_t>(p) * K + c * 32;
+      float sum = 0.0f;
+      uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 q = ld16(src + v * 8);
+        sum += bf16lo(q.x) + bf16hi(q.x) + bf16lo(q.y) + bf16hi(q.y) + bf16lo(q.z) +
+               bf16hi(q.z) + bf16lo(q.w) + bf16hi(q.w);
+        dst[v] = pair_permute(q);
+      }
+      csum[m * C + c] = sum;
+    }
+    __syncthreads();
+
+    float acc0[MAXM], acc1[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc0[m] = acc1[m] = 0.0f;
+
+    for (int cb = lk; cb < C; cb += 4 * LK) {
+      uint4 q0[4], q1[4];
+      float s0[4], s1[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = cb + b * LK;
+        if (c < C) {
+          q0[b] = ld16(W0 + c * 16);
+          q1[b] = ld16(W1 + c * 16);
+          s0[b] = fp16_bits_to_f32(S0[c >> 2]);
+          s1[b] = fp16_bits_to_f32(S1[c >> 2]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = cb + b * LK;
+        if (c < C) {
+#pragma unroll
+          for (int m = 0; m < MAXM; ++m) {
+            if (m < Mc) {
+              const uint4* xp = reinterpret_cast<const uint4*>(xs + m * (K / 2) + c * 16);
+              const float cs = kCodeBias * csum[m * C + c];
+              float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const uint4 xv = xp[v];
+                const uint32_t w0 = (&q0[b].x)[v], w1 = (&q1[b].x)[v];
+                uint32_t a0, a1, a2, a3;
+                nibble_pairs(w0, a0, a1, a2, a3);
+                d0 = dot2_bf16(a0, xv.x, d0);
+                d0 = dot2_bf16(a1, xv.y, d0);
+                d0 = dot2_bf16(a2, xv.z, d0);
+                d0 = dot2_bf16(a3, xv.w, d0);
+                nibble_pairs(w1, a0, a1, a2, a3);
+                d1 = dot2_bf16(a0, xv.x, d1);
+                d1 = dot2_bf16(a1, xv.y, d1);
+                d1 = dot2_bf16(a2, xv.z, d1);
+                d1 = dot2_bf16(a3, xv.w, d1);
+              }
+              acc0[m] += s0[b] * (d0 - cs);
+              acc1[m] += s1[b] * (d1 - cs);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int sh = LK / 2; sh >= 1; sh >>= 1) {
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        acc0[m] += wave_shfl_xor(acc0[m], sh);
+        acc1[m] += wave_shfl_xor(acc1[m], sh);
+      }
+    }
+    if (lk == 0 && valid) {
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        if (m < Mc) {
+          const size_t p = static_cast<size_t>(p0 + m0 + m);
+          if (KIND == 0) {
+            out[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0[m], acc1[m]));
+          } else {
+            *reinterpret_cast<uint32_t*>(out + p * N + 2 * u) = pack_bf16x2(acc0[m], acc1[m]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // LDS is restaged by the next row chunk
+  }
+}
+
+template <int KIND, int LK, int MAXM>
+hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                         const int* offsets, const int* sorted_slot, const int* active,
+                         const int* n_active, uint16_t* out, int K, int N, int topk,
+                         int max_active, hipStream_t s) {
+  constexpr int UB = (kThreads / kWave) * (kWave / LK);
+  const int units = N / 2;
+  const int tiles = (units + UB - 1) / UB;
+  const size_t lds = static_cast<size_t>(MAXM) * (K / 2) * 4 + static_cast<size_t>(MAXM) * (K / 32) * 4;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&w4a16_gemv_kernel<KIND, LK, MAXM>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, LK, MAXM>), dim3(max_active * tiles),
+                     dim3(kThreads), lds, s, A, W, S, offsets, sorted_slot, active, n_active,
+                     out, K, N, topk, tiles);
+  return hipGetLastError();
+}
+
+template <int KIND, int MAXM>
+hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                       const int* offsets, const int* sorted_slot, const int* active,
+                       const int* n_active, uint16_t* out, int K, int N, int topk,
+                       int max_active, hipStream_t s) {
+  const int C = K / 32;
+  if (C % 16 == 0 && C >= 64)
+    return launch_gemv_t<KIND, 16, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out,
+                                         K, N, topk, max_active, s);
+  if (C % 8 == 0)
+    return launch_gemv_t<KIND, 8, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out,
+                                        K, N, topk, max_active, s);
+  return launch_gemv_t<KIND, 4, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out, K,
+                                      N, topk, max_active, s);
+}
+
+// ---------------------------------------------------------------- MFMA ----
+constexpr int kALd = kGroup + 8;  // LDS row stride of the activation tile (bf16)
+
+// KIND 0: gate/up. Wave w owns h-columns [nt*128 + 32w, +32): B subtile 0 is
+//         gate rows, subtile 1 the matching up rows.
+// KIND 1: down. Wave w owns W2 rows [nt*256 + 64w, +64) as two subtiles.
+// Operand k order: within each 16-k MFMA step, lane half hf = lane/32 takes
+// k = 64*hf + 8*s + {0,4,1,5,2,6,3,7} (s = step); A is stored in LDS in that
+// pair order, B comes out of nibble_pairs() in it.
+template <int KIND, int MT>
+__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
+    const uint16_t* __restrict__ S, const int* __restrict__ offsets,
+    const int* __restrict__ sorted_slot, uint16_t* __restrict__ out, int K, int N, int E,
+    int topk, int NT) {
+  constexpr int BM = 32 * MT;
+  constexpr int CPT = BM * 16 / kThreads;  // 16-byte A chunks per thread per group
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * kALd];
+  __shared__ __attribute__((aligned(16))) float c_lds[2][BM];
+  __shared__ int sm_pref[kThreads / kWave];
+  __shared__ int sm_out[3];
+
+  TileInfo ti;
+  if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int G = K / kGroup;
+  const size_t rowb = static_cast<size_t>(K / 2);
+
+  // B rows of this lane (two subtiles)
+  int nrow[2];
+  bool nvalid[2];
+  if (KIND == 0) {
+    const int n = ti.nt * 128 + wv * 32 + l32;  // h column
+    nvalid[0] = nvalid[1] = n < N / 2;
+    const int nc = nvalid[0] ? n : N / 2 - 1;
+    nrow[0] = nc;
+    nrow[1] = N / 2 + nc;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = ti.nt * 256 + wv * 64 + j * 32 + l32;
+      nvalid[j] = n < N;
+      nrow[j] = nvalid[j] ? n : N - 1;
+    }
+  }
+  const uint8_t* Wr[2];
+  const uint16_t* Sr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    Wr[j] = W + (static_cast<size_t>(ti.e) * N + nrow[j]) * rowb + hf * 32;
+    Sr[j] = S + (static_cast<size_t>(ti.e) * N + nrow[j]) * G;
+  }
+
+  // A rows staged by this thread: chunk q = tid + 256*v -> row q/16, chunk q%16
+  const uint16_t* arow[CPT];
+#pragma unroll
+  for (int v = 0; v < CPT; ++v) {
+    const int q = tid + kThreads * v;
+    const int r = q >> 4, ch = q & 15;
+    const int p = ti.p_begin + r;
+    if (p < ti.p_end) {
+      const size_t src = (KIND == 0) ? static_cast<size_t>(sorted_slot[p] / topk) : static_cast<size_t>(p);
+      arow[v] = A + src * K + ch * 8;
+    } else {
+      arow[v] = nullptr;
+    }
+  }
+
+  auto load_a = [&](int g, uint4* regs) {
+#pragma unroll
+    for (int v = 0; v < CPT; ++v)
+      regs[v] = arow[v] ? ld16(arow[v] + g * kGroup) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_a = [&](int buf, const uint4* regs) {
+#pragma unroll
+    for (int v = 0; v < CPT; ++v) {
+      const int q = tid + kThreads * v;
+      const int r = q >> 4, ch = q & 15;
+      const uint4 x = regs[v];
+      float sum = bf16lo(x.x) + bf16hi(x.x) + bf16lo(x.y) + bf16hi(x.y) + bf16lo(x.z) +
+                  bf16hi(x.z) + bf16lo(x.w) + bf16hi(x.w);
+#pragma unroll
+      for (int sh = 8; sh >= 1; sh >>= 1) sum += wave_shfl_xor(sum, sh);
+      *reinterpret_cast<uint4*>(&a_lds[buf][r * kALd + ch * 8]) = pair_permute(x);
+      if (ch == 0) c_lds[buf][r] = kCodeBias * sum;
+    }
+  };
+  auto load_b = [&](int g, uint4 (&bq)[2][2], float (&bs)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bq[j][0] = ld16(Wr[j] + g * 64);
+      bq[j][1] = ld16(Wr[j] + g * 64 + 16);
+      bs[j] = fp16_bits_to_f32(Sr[j][g]);
+    }
+  };
+
+  f32x16_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  uint4 areg[CPT];
+  uint4 bq[2][2], bq_next[2][2];
+  float bs[2], bs_next[2];
+  load_a(0, areg);
+  store_a(0, areg);
+  load_b(0, bq, bs);
+  __syncthreads();
+
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    const bool more = g + 1 < G;
+    if (more) {
+      load_a(g + 1, areg);
+      load_b(g + 1, bq_next, bs_next);
+    }
+    f32x16_t accg[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accg[i][j][r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8_t bop[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = (&bq[j][s >> 2].x)[s & 3];
+        uint4 p;
+        nibble_pairs(w, p.x, p.y, p.z, p.w);
+        bop[j] = __builtin_bit_cast(bf16x8_t, p);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const uint4 av = *reinterpret_cast<const uint4*>(
+            &a_lds[buf][(i * 32 + l32) * kALd + hf * 64 + s * 8]);
+        const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[j], accg[i][j], 0, 0, 0);
+      }
+    }
+    // scale and un-bias the group's partial sums
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const float4 cb = *reinterpret_cast<const float4*>(&c_lds[buf][i * 32 + rb * 8 + hf * 4]);
+        const float cv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            acc[i][j][rb * 4 + r4] += bs[j] * (accg[i][j][rb * 4 + r4] - cv[r4]);
+      }
+    }
+    if (more) {
+      store_a(buf ^ 1, areg);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bq[j][0] = bq_next[j][0];
+        bq[j][1] = bq_next[j][1];
+        bs[j] = bs_next[j];
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: C layout of 32x32 MFMA: lane holds column l32, rows
+  // 8*(r/4) + 4*hf + (r%4), r = 0..15
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+      const int p = ti.p_begin + m;
+      if (p >= ti.p_end) continue;
+      if (KIND == 0) {
+        if (nvalid[0]) {
+          const int n = ti.nt * 128 + wv * 32 + l32;
+          out[static_cast<size_t>(p) * (N / 2) + n] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (nvalid[j])
+            out[static_cast<size_t>(p) * N + nrow[j]] = f32_to_bf16(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+template <int KIND, int MT>
+hipError_t launch_mfma_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                         const int* offsets, const int* sorted_slot, uint16_t* out, int K, int N,
+                         int E, int topk, int T, hipStream_t s) {
+  constexpr int BM = 32 * MT;
+  const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + 255) / 256;
+  const long long R = static_cast<long long>(T) * topk;
+  const long long act = R < E ? R : E;
+  // upper bound of m-tiles: sum over active experts of ceil(rows / BM)
+  const long long mt_up = (R + BM - 1) / BM + act;
+  long long grid = mt_up * NT;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((w4a16_mfma_kernel<KIND, MT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, s, A, W, S, offsets, sorted_slot, out, K, N, E, topk, NT);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool w4a16_uses_gemv(int T, int, int, int, int) { return T <= kGemvMaxT; }
+
+size_t w4a16_workspace_bytes(int T, int, int I, int, int k) {
+  return align_up(static_cast<size_t>(T) * k * I * sizeof(uint16_t), 256);
+}
+
+hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
+                            const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
+                            const uint16_t* s2, const int* offsets, const int* sorted_slot,
+                            const int* active, const int* n_active, uint16_t* y, void* ws,
+                            hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  uint16_t* h = static_cast<uint16_t*>(ws);
+  const int R = T * k;
+  const int max_active = R < E ? R : E;
+  hipError_t err;
+  if (T <= kGemvMaxT) {
+    if (T <= 2) {
+      err = launch_gemv<0, 2>(x, w13, s13, offsets, sorted_slot, active, n_active, h, H, 2 * I, k,
+                              max_active, s);
+      if (err != hipSuccess) return err;
+      return launch_gemv<1, 2>(h, w2, s2, offsets, sorted_slot, active, n_active, y, I, H, k,
+                               max_active, s);
+    }
+    err = launch_gemv<0, 4>(x, w13, s13, offsets, sorted_slot, active, n_active, h, H, 2 * I, k,
+                            max_active, s);
+    if (err != hipSuccess) return err;
+    return launch_gemv<1, 4>(h, w2, s2, offsets, sorted_slot, active, n_active, y, I, H, k,
+                             max_active, s);
+  }
+  const double avg_rows = static_cast<double>(R) / max_active;
+  if (avg_rows <= 48.0) {
+    err = launch_mfma_t<0, 1>(x, w13, s13, offsets, sorted_slot, h, H, 2 * I, E, k, T, s);
+    if (err != hipSuccess) return err;
+    return launch_mfma_t<1, 1>(h, w2, s2, offsets, sorted_slot, y, I, H, E, k, T, s);
+  }
+  err = launch_mfma_t<0, 2>(x, w13, s13, offsets, sorted_slot, h, H, 2 * I, E, k, T, s);
+  if (err != hipSuccess) return err;
+  return launch_mfma_t<1, 2>(h, w2, s2, offsets, sorted_slot, y, I, H, E, k, T, s);
+}
+
+}  // namespace moe

@@ -17,6 +17,8 @@ Formats produced (the layer's storage formats, not its arithmetic):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -145,9 +147,11 @@ def layer_w4(wl: Workload, unit: int, experts=None):
     s13 = np.zeros((E, 2 * wl.I, wl.H // GROUP), np.uint16)
     w2 = np.zeros((E, wl.H, wl.I // 2), np.uint8)
     s2 = np.zeros((E, wl.H, wl.I // GROUP), np.uint16)
-    for e in (range(E) if experts is None else experts):
+
+    def fill(e):
         w13[e], s13[e] = expert_w4(wl, unit, e, "w13")
         w2[e], s2[e] = expert_w4(wl, unit, e, "w2")
+    _parallel(fill, range(E) if experts is None else [int(e) for e in experts])
     return w13, s13, w2, s2
 
 
@@ -158,7 +162,17 @@ def layer_w8(wl: Workload, unit: int):
     s13 = np.empty((E, 2 * wl.I), np.float32)
     w2 = np.empty((E, wl.H, wl.I), np.int8)
     s2 = np.empty((E, wl.H), np.float32)
-    for e in range(E):
+
+    def fill(e):
         w13[e], s13[e] = expert_w8(wl, unit, e, "w13")
         w2[e], s2[e] = expert_w8(wl, unit, e, "w2")
+    _parallel(fill, range(E))
     return w13, s13, w2, s2
+
+
+def _parallel(fn, items) -> None:
+    """Run fn over items on a few threads (numpy's generators release the GIL
+    for bulk draws); each item writes its own slice, so order does not matter."""
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fn, items))

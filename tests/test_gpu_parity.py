@@ -1,0 +1,294 @@
+"""GPU parity: every step of the layer through the C ABI against the CPU oracle
+on the same seeded inputs. Integers (ids, permutation, W8A8 codes and int32
+accumulators) bit-exact; floats within the layer tolerance."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from gpu_util import (assert_close, check_routing_and_perm, expert_getter_w4,  # noqa: E402
+                      expert_getter_w8, run_layer, stage_weights, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_expert_top_amd as moe
+    moe.load()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ----------------------------------------------------------------- routing --
+def _route_gpu(L, k):
+    import quantized_moe_expert_top_amd as moe
+    T, E = L.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.route_topk(to_dev(np.ascontiguousarray(L, np.float32)), k, ids, w)
+    torch.cuda.synchronize()
+    return to_np(ids), to_np(w)
+
+
+@pytest.mark.parametrize("name,unit", [("tiny", 0), ("decode_t2", 0), ("decode_t2", 7),
+                                       ("prefill_t512", 0), ("w8a8_t4096", 0),
+                                       ("decode_large", 3)])
+def test_route_workloads(name, unit):
+    wl = synth.workload(name)
+    _say("route", name, unit, wl.T, wl.E, wl.k)
+    L = synth.router_logits(wl, unit)
+    ids, w = _route_gpu(L, wl.k)
+    rids, rw = oracle.route_topk(L, wl.k)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=0, atol=1e-6)
+
+
+def test_route_hand_cases_and_ties():
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "route_hand.json")))
+    for c in cases["cases"]:
+        L = np.array(c["logits"], np.float32)
+        ids, w = _route_gpu(L, c["k"])
+        np.testing.assert_array_equal(ids, c["ids"])
+        np.testing.assert_allclose(w, c["w"], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("T,E,k", [(33, 1024, 32), (64, 1, 1), (17, 256, 8), (5, 64, 64 // 2),
+                                   (9, 300, 7)])
+def test_route_forced_ties_and_extremes(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    L[L == 0] = np.where(rng.random(np.count_nonzero(L == 0)) < 0.5, 0.0, -0.0)
+    _say("route ties", T, E, k)
+    ids, w = _route_gpu(L, k)
+    rids, rw = oracle.route_topk(L, k)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=0, atol=1e-6)
+
+
+# ------------------------------------------------------------- permutation --
+def _permute_gpu(ids, E):
+    import quantized_moe_expert_top_amd as moe
+    T, k = ids.shape
+    R = T * k
+    d = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")  # noqa: E731
+    off, ss, sp, act, na = d(E + 1), d(R), d(R), d(min(E, R)), d(1)
+    ws = torch.empty(max(moe.permute_workspace(T, E, k), 16), dtype=torch.uint8, device="cuda")
+    moe.permute(to_dev(np.ascontiguousarray(ids, np.int32)), E, off, ss, sp, act, na, ws)
+    torch.cuda.synchronize()
+    n = int(to_np(na)[0])
+    return {"expert_offsets": to_np(off)[:E + 1], "sorted_slot": to_np(ss)[:R],
+            "slot_pos": to_np(sp)[:R], "active": to_np(act)[:n], "n_active": n}
+
+
+def _random_ids(T, E, k, seed, skew=0.0):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)) - skew * np.log(np.arange(1, E + 1))
+    return oracle.route_topk(logits.astype(np.float32), k)[0]
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(16, 8, 2, 0), (2, 128, 8, 0), (129, 128, 8, 0),
+                                        (4096, 128, 8, 0), (4096, 128, 8, 2.0), (64, 1024, 32, 0),
+                                        (1, 1, 1, 0), (1000, 3, 3, 0), (300, 256, 8, 1.1)])
+def test_permute_matches_oracle(T, E, k, skew):
+    ids = _random_ids(T, E, k, T + E, skew)
+    _say("permute", T, E, k, skew)
+    got = _permute_gpu(ids, E)
+    ref = oracle.permute(ids, E)
+    for key in ("expert_offsets", "sorted_slot", "slot_pos", "active"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    assert got["n_active"] == ref["n_active"]
+
+
+def test_permute_empty_batch():
+    got = _permute_gpu(np.zeros((0, 4), np.int32), 16)
+    assert np.all(got["expert_offsets"] == 0) and got["n_active"] == 0
+
+
+# ----------------------------------------------------------------- combine --
+def test_combine_matches_oracle():
+    import quantized_moe_expert_top_amd as moe
+    rng = np.random.default_rng(1)
+    T, H, k = 77, 520, 5
+    ybits = synth.bf16_bits_from_f32(rng.standard_normal((T * k, H)).astype(np.float32))
+    slot_pos = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.combine(to_dev(ybits), to_dev(slot_pos), to_dev(w), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(oracle.bf16_to_f64(ybits), slot_pos, w.astype(np.float64))
+    np.testing.assert_allclose(to_np(out), ref, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------ W4A16 layer --
+def _w4_layer_case(wl, unit=0, logits=None, only_routed=True):
+    x = synth.x_bf16(wl, unit)
+    L = synth.router_logits(wl, unit) if logits is None else logits
+    ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, unit))
+    experts = ref["perm"]["active"] if only_routed else None
+    _say("w4a16 layer", wl.name, unit, (wl.T, wl.H, wl.I, wl.E, wl.k))
+    res = run_layer(wl, x, L, stage_weights(wl, unit, experts))
+    check_routing_and_perm(res, ref)
+    s1 = assert_close(res["y"], ref["y"], "y")
+    s2 = assert_close(res["out"], ref["out"], "out")
+    return res, ref, s1, s2
+
+
+CUSTOM_W4 = [
+    # name, wid, T, H, I, E, k : ragged and edge shapes on both kernels
+    ("gemv_t1", 101, 1, 256, 128, 8, 2),
+    ("gemv_t3_ragged", 102, 3, 384, 384, 16, 4),       # K=384: 12 chunks -> 4 lanes per row
+    ("gemv_t4", 103, 4, 1280, 640, 32, 6),
+    ("mfma_t5", 104, 5, 256, 128, 8, 2),
+    ("mfma_t37_ragged", 105, 37, 640, 384, 12, 3),     # 5 groups, I not a multiple of 256
+    ("mfma_t300_dense", 106, 300, 256, 256, 4, 2),     # >64 rows per expert: m-tile loop
+    ("e1_k1", 107, 9, 256, 128, 1, 1),
+    ("k_equals_e", 108, 6, 256, 128, 4, 4),
+]
+
+
+@pytest.mark.parametrize("case", CUSTOM_W4, ids=[c[0] for c in CUSTOM_W4])
+def test_w4a16_custom_shapes(case):
+    name, wid, T, H, I, E, k = case
+    wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
+    _w4_layer_case(wl, only_routed=False)
+
+
+@pytest.mark.parametrize("name,unit", [("tiny", 0), ("decode_t2", 0), ("decode_t2", 31),
+                                       ("prefill_t512", 0), ("prefill_t512", 5)])
+def test_w4a16_workload_layers(name, unit):
+    wl = synth.workload(name)
+    _w4_layer_case(wl, unit)
+
+
+def test_w4a16_decode_large_steps():
+    wl = synth.workload("decode_large")
+    for step in (0, 9):
+        _w4_layer_case(wl, step)
+
+
+@pytest.mark.parametrize("T", [4, 300])
+def test_w4a16_all_tokens_one_expert(T):
+    """Degenerate routing: every token's top pick is expert 3 (one expert holds T rows)."""
+    wl = synth.Workload(f"skew_t{T}", 120 + T, T, 512, 256, 16, 2, "w4a16", "none", 1)
+    L = synth.router_logits(wl, 0).astype(np.float64)
+    L[:, 3] += 50.0
+    _w4_layer_case(wl, logits=L.astype(np.float32), only_routed=False)
+
+
+def test_w4a16_zero_inputs_give_zero():
+    wl = synth.Workload("zeros", 130, 8, 256, 128, 8, 2, "w4a16", "none", 1)
+    x = np.zeros((wl.T, wl.H), np.uint16)
+    L = synth.router_logits(wl, 0)
+    res = run_layer(wl, x, L, stage_weights(wl, 0))
+    assert np.all(res["out"] == 0.0)
+    for T in (2, 8):   # down codes all 8 -> exact zeros, on both kernels
+        wl2 = wl.with_(T=T)
+        w13, s13, w2, s2 = synth.layer_w4(wl2, 0)
+        w2[:] = 0x88
+        res = run_layer(wl2, synth.x_bf16(wl2, 0), synth.router_logits(wl2, 0),
+                        tuple(to_dev(a) for a in (w13, s13, w2, s2)))
+        assert np.all(res["out"] == 0.0)
+
+
+def test_w4a16_deterministic():
+    for name in ("tiny", "prefill_t512", "decode_t2"):
+        wl = synth.workload(name)
+        x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+        wts = stage_weights(wl, 0)
+        a = run_layer(wl, x, L, wts)
+        b = run_layer(wl, x, L, wts)
+        np.testing.assert_array_equal(a["y_bits"], b["y_bits"])
+        np.testing.assert_array_equal(a["out_bits"], b["out_bits"])
+
+
+# ------------------------------------------------------------- W8A8 layer --
+def _check_w8a8(res, ref, w2_getter):
+    np.testing.assert_array_equal(res["xq"], ref["xq"])
+    np.testing.assert_array_equal(res["xs"].view(np.uint32), ref["xs"].view(np.uint32))
+    np.testing.assert_array_equal(res["acc13"], ref["acc13"])
+    # h codes: decided in float32 on both sides from float32 h that differ by
+    # rounding only; a code may differ by one step, and only at a .5 boundary
+    dq = res["hq"].astype(np.int32) - ref["hq"].astype(np.int32)
+    assert np.all(np.abs(dq) <= 1)
+    assert np.count_nonzero(dq) <= 1e-3 * dq.size + 1
+    np.testing.assert_allclose(res["hs"], ref["hs"], rtol=1e-5, atol=0)
+    if np.count_nonzero(dq):
+        v = np.abs(ref["h"] / np.where(ref["hs"] > 0, ref["hs"], 1)[:, None])
+        near = np.abs(v - np.floor(v) - 0.5) < 1e-3
+        assert np.all(near[dq != 0])
+    # down accumulators: exact where the codes agree; elsewhere the difference
+    # is exactly the integer product of the code difference
+    same = ~np.any(dq != 0, axis=1)
+    np.testing.assert_array_equal(res["acc2"][same], ref["acc2"][same])
+    off = ref["perm"]["expert_offsets"]
+    for p in np.nonzero(~same)[0]:
+        e = int(np.searchsorted(off, p, side="right") - 1)
+        w2 = w2_getter(e)
+        want = ref["acc2"][p] + w2.astype(np.int64) @ dq[p].astype(np.int64)
+        np.testing.assert_array_equal(res["acc2"][p], want)
+    s1 = assert_close(res["y"], ref["y"], "y")
+    s2 = assert_close(res["out"], ref["out"], "out")
+    return s1, s2
+
+
+def _w8_case(wl, unit=0):
+    x = synth.x_bf16(wl, unit)
+    L = synth.router_logits(wl, unit)
+    get = expert_getter_w8(wl, unit)
+    ref = oracle.moe_layer_w8a8(x, L, wl.k, get)
+    _say("w8a8 layer", wl.name, unit, (wl.T, wl.H, wl.I, wl.E, wl.k))
+    res = run_layer(wl, x, L, stage_weights(wl, unit), debug=True)
+    check_routing_and_perm(res, ref)
+    return _check_w8a8(res, ref, lambda e: get(e)[2])
+
+
+CUSTOM_W8 = [
+    ("w8_small", 201, 64, 256, 128, 8, 2),
+    ("w8_ragged", 202, 45, 192, 320, 6, 3),   # K=192/320: not multiples of 128
+    ("w8_t1", 203, 1, 128, 64, 4, 1),
+    ("w8_many_rows", 204, 700, 256, 128, 4, 2),   # >128 rows per expert
+]
+
+
+@pytest.mark.parametrize("case", CUSTOM_W8, ids=[c[0] for c in CUSTOM_W8])
+def test_w8a8_custom_shapes(case):
+    name, wid, T, H, I, E, k = case
+    _w8_case(synth.Workload(name, wid, T, H, I, E, k, "w8a8", "none", 1))
+
+
+def test_w8a8_full_layer_t4096():
+    _w8_case(synth.workload("w8a8_t4096"), 1)
+
+
+def test_w8a8_zero_token_row():
+    wl = synth.Workload("w8_zero_row", 205, 12, 256, 128, 8, 2, "w8a8", "none", 1)
+    x = synth.x_bf16(wl, 0)
+    x[5] = 0
+    L = synth.router_logits(wl, 0)
+    get = expert_getter_w8(wl, 0)
+    ref = oracle.moe_layer_w8a8(x, L, wl.k, get)
+    res = run_layer(wl, x, L, stage_weights(wl, 0), debug=True)
+    assert res["xs"][5] == 0 and np.all(res["xq"][5] == 0)
+    assert np.all(res["out"][5] == 0)
+    _check_w8a8(res, ref, lambda e: get(e)[2])
+
+
+def test_empty_batch_all_entry_points():
+    import quantized_moe_expert_top_amd as moe
+    for fmt in ("w4a16", "w8a8"):
+        b = moe.LayerBuffers.alloc(0, 256, 128, 8, 2, fmt)
+        x = torch.empty((0, 256), dtype=torch.int16, device="cuda")
+        L = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+        dummy = torch.empty(16, dtype=torch.uint8, device="cuda")
+        moe.moe_forward(b, x, L, (dummy, dummy, dummy, dummy))
+        torch.cuda.synchronize()
+        assert np.all(to_np(b.offsets) == 0) and int(to_np(b.n_active)[0]) == 0
