@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_t2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of HIP graphs")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     return ap.parse_args()
 
@@ -90,46 +91,76 @@ def main():
     moe.load()
     wl = synth.workload(args.workload)
     units = stage(wl, torch)
-    b = moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    bufs = [moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt) for _ in range(wl.units)]
     shape = (wl.T, wl.H, wl.I, wl.E, wl.k)
     ffn = moe.grouped_w4a16_ffn if wl.fmt == "w4a16" else moe.grouped_w8a8_ffn
     schedule = layers_per_step(wl)
-    stream = torch.cuda.current_stream()
 
-    def layer(u, ev=None):
-        x, L, (w13, s13, w2, s2) = units[u]
+    def ffn_call(u):
+        x, _, (w13, s13, w2, s2) = units[u]
+        b = bufs[u]
+        ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active, b.n_active, b.y,
+            b.ffn_ws)
+
+    def layer(u):
+        x, L, _ = units[u]
+        b = bufs[u]
         moe.route_topk(L, wl.k, b.ids, b.w)
         moe.permute(b.ids, wl.E, b.offsets, b.sorted_slot, b.slot_pos, b.active, b.n_active,
                     b.perm_ws)
-        if ev is not None:
-            ev[0].record(stream)
-        ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active, b.n_active, b.y,
-            b.ffn_ws)
-        if ev is not None:
-            ev[1].record(stream)
+        ffn_call(u)
         moe.combine(b.y, b.slot_pos, b.w, b.out)
 
-    def step(i, events=None):
-        for u in schedule[i % len(schedule)]:
-            ev = None
-            if events is not None:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                events.append((u, ev))
-            layer(u, ev)
+    # one eager pass: checks the device once, leaves every unit's routing in place
+    for u in range(wl.units):
+        layer(u)
+    torch.cuda.synchronize()
+    act_per_unit = {u: int(bufs[u].n_active.cpu()[0]) for u in range(wl.units)}
 
+    # one HIP graph per step (the whole path for every layer of the step), and
+    # one per step holding only the grouped-FFN calls (the dominant kernel)
+    step_graphs, ffn_graphs = [], []
+    if not args.eager:
+        for us in schedule:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for u in us:
+                    layer(u)
+            step_graphs.append(g)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for u in us:
+                    ffn_call(u)
+            ffn_graphs.append(g)
+
+    def run_step(i):
+        if args.eager:
+            for u in schedule[i % len(schedule)]:
+                layer(u)
+        else:
+            step_graphs[i % len(schedule)].replay()
+
+    def run_ffn(i):
+        if args.eager:
+            for u in schedule[i % len(schedule)]:
+                ffn_call(u)
+        else:
+            ffn_graphs[i % len(schedule)].replay()
+
+    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        step(i)
+        run_step(i)
+        run_ffn(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, with HIP events around every grouped-FFN call
-    events = []
+    # timed region: exactly K steps of the whole path
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events)
+        run_step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -137,23 +168,22 @@ def main():
     ms_per_step = ms_total / args.steps
     value = wl.T * args.steps / (ms_total / 1e3)   # each step carries T tokens
 
-    # algorithmic bytes of each grouped-FFN call: routed experts' weights + x + y
-    act_per_unit = {}
-    for u in range(wl.units):
-        layer(u)
-        torch.cuda.synchronize()
-        act_per_unit[u] = int(b.n_active.cpu()[0])
+    # dominant kernel: the grouped FFN calls of the same K steps, back to back
+    # on the same stream, timed with HIP events
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for i in range(args.steps):
+        run_ffn(i)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
+    avg_ms = f0.elapsed_time(f1) / len(calls)
     eb = expert_bytes(wl)
-    io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 2
-    tot_bytes, tot_ms = 0.0, 0.0
-    for u, (e0, e1) in events:
-        tot_bytes += act_per_unit[u] * eb + io_bytes
-        tot_ms += e0.elapsed_time(e1)
-    n_calls = len(events)
-    avg_ms = tot_ms / n_calls
-    avg_bytes = tot_bytes / n_calls
+    io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 4   # x in (bf16), y out (float32)
+    avg_bytes = sum(act_per_unit[u] * eb + io_bytes for u in calls) / len(calls)
     achieved = avg_bytes / (avg_ms / 1e3) / 1e9
-    flops_per_call = 2.0 * 3 * wl.H * wl.I * wl.T * wl.k
+    flops_per_call = 6.0 * wl.H * wl.I * wl.T * wl.k
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -161,7 +191,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": None,
-        "kernel": f"moe_grouped_{wl.fmt}_ffn (gate/up + down)",
+        "kernel": f"moe_grouped_{wl.fmt}_ffn (gate/up + down kernels)",
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "algo_bytes_per_launch": int(avg_bytes),
     }
@@ -186,6 +216,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "format": "W4A16 g128" if wl.fmt == "w4a16" else "W8A8",
                    "layers_per_step": len(schedule[0]),
+                   "launch": "eager" if args.eager else "hip_graph_per_step",
                    "mean_active_experts": round(float(np.mean(list(act_per_unit.values()))), 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -127,7 +127,7 @@ typedef struct {
  * p and t = sorted_slot[p] / k:
  *   gate = x[t] . W13[e][n]^T,  up = x[t] . W13[e][I + n]^T   (n < I)
  *   h[p, n] = silu(gate) * up
- *   y[p, :] = h[p] . W2[e]^T                       (stored bf16, grouped order)
+ *   y[p, :] = h[p] . W2[e]^T                    (stored float32, grouped order)
  * Weight format: codes packed two per byte along K (low nibble = even k),
  * implicit zero point 8, one fp16 scale per (output row, 128-wide K group):
  *   W[n, k] = (q[n, k] - 8) * scale[n, k / 128].
@@ -135,8 +135,9 @@ typedef struct {
  *   w13 uint8 [E, 2I, H/2]     s13 fp16 [E, 2I, H/128]   (rows [0,I) gate, [I,2I) up)
  *   w2  uint8 [E, H, I/2]      s2  fp16 [E, H, I/128]
  *   expert_offsets, sorted_slot, active, n_active: as written by moe_permute.
- *   y   bf16  [T*k, H]         (output, grouped order)
- * Accumulation is float32; h is rounded to bf16 between the two projections.
+ *   y   float32 [T*k, H]       (output, grouped order)
+ * Accumulation is float32; h is rounded to bf16 between the two projections
+ * (it is the bf16 MFMA operand of the down projection); y stays float32.
  * Requires H % 128 == 0, I % 128 == 0. `ws` must hold
  * moe_w4a16_workspace(shape) bytes. Small T runs a register-dequant grouped
  * GEMV; larger T a bf16 MFMA grouped GEMM; both meet the same tolerance.
@@ -147,7 +148,7 @@ MOE_API int moe_grouped_w4a16_ffn(const moe_shape* shape, const uint16_t* x,
                           const uint8_t* w2, const uint16_t* s2,
                           const int32_t* expert_offsets, const int32_t* sorted_slot,
                           const int32_t* active, const int32_t* n_active,
-                          uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+                          float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Optional W8A8 intermediate outputs (device pointers; any may be NULL). */
 typedef struct {
@@ -170,9 +171,9 @@ typedef struct {
  *   h[p, n] = silu(gate) * up       (float32), quantized per row by the same
  *                                   rule -> hq[p, :], hs[p]
  *   acc2[p, m] = sum_n hq[p, n] * w2[e, m, n]                (exact int32)
- *   y[p, m] = acc2[p, m] * hs[p] * s2[e, m]                  (stored bf16)
+ *   y[p, m] = acc2[p, m] * hs[p] * s2[e, m]                  (float32)
  *   x   bf16 [T, H]; w13 int8 [E, 2I, H], s13 float32 [E, 2I];
- *   w2  int8 [E, H, I], s2 float32 [E, H]; y bf16 [T*k, H] (grouped order).
+ *   w2  int8 [E, H, I], s2 float32 [E, H]; y float32 [T*k, H] (grouped order).
  * Requires H % 64 == 0, I % 64 == 0. `dbg` may be NULL; non-NULL members
  * receive the intermediates. `ws` must hold moe_w8a8_workspace(shape) bytes.
  */
@@ -182,18 +183,18 @@ MOE_API int moe_grouped_w8a8_ffn(const moe_shape* shape, const uint16_t* x,
                          const int8_t* w2, const float* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
                          const int32_t* active, const int32_t* n_active,
-                         uint16_t* y, const moe_w8a8_debug* dbg,
+                         float* y, const moe_w8a8_debug* dbg,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine — weighted sum of each token's k expert outputs.
  * out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[slot_pos[t*k + j], :],
  * accumulated in float32 in increasing j (fixed order, no atomics).
- *   y bf16 [T*k, H] (grouped order), slot_pos int32 [T*k], topk_w float32 [T, k],
- *   out float32 [T, H].
+ *   y float32 [T*k, H] (grouped order), slot_pos int32 [T*k],
+ *   topk_w float32 [T, k], out float32 [T, H].
  * Requires H % 8 == 0.
  */
-MOE_API int moe_combine(const uint16_t* y, const int32_t* slot_pos, const float* topk_w,
+MOE_API int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w,
                 int32_t T, int32_t H, int32_t k, float* out, void* stream);
 
 #ifdef __cplusplus

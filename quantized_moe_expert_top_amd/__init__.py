@@ -57,7 +57,7 @@ class LayerBuffers:
             n_active=torch.empty(4, **i32),
             perm_ws=torch.empty(max(pws, 16), dtype=torch.uint8, device=device),
             ffn_ws=torch.empty(max(fws, 16), dtype=torch.uint8, device=device),
-            y=torch.empty((max(R, 1), H), dtype=torch.int16, device=device),
+            y=torch.empty((max(R, 1), H), dtype=torch.float32, device=device),
             out=torch.empty((T, H), dtype=torch.float32, device=device),
         )
 

@@ -49,7 +49,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"libmoe.so not built at {path}; run __graft_entry__.build() or "
                            "python -m quantized_moe_expert_top_amd.build")
+    # libmoe must bind to the HIP runtime that owns the process's device memory
+    # and streams. torch ships its own libamdhip64 (same soname as ROCm's), so
+    # import it first: the dynamic loader then reuses that copy instead of
+    # mapping a second HIP/HSA runtime from ROCm's directory.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes mapped in this process: {runtimes}")
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -71,6 +79,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = args
     _lib = lib
     return lib
+
+
+def _hip_runtimes_mapped() -> list:
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
 
 
 def _check(fn: str, status: int) -> None:
@@ -145,7 +161,7 @@ def _check_ffn_sizes(shape, x, expert_offsets, sorted_slot, active, n_active, y)
     _need(sorted_slot, R * 4, "sorted_slot")
     _need(active, min(E, R) * 4, "active")
     _need(n_active, 4, "n_active")
-    _need(y, R * H * 2, "y")
+    _need(y, R * H * 4, "y")
 
 
 def grouped_w4a16_ffn(shape, x, w13, s13, w2, s2, expert_offsets, sorted_slot, active,
@@ -199,7 +215,7 @@ def grouped_w8a8_ffn(shape, x, w13, s13, w2, s2, expert_offsets, sorted_slot, ac
 def combine(y, slot_pos, topk_w, out, stream=None) -> None:
     T, k = topk_w.shape
     H = y.shape[1]
-    _need(y, T * k * H * 2, "y")
+    _need(y, T * k * H * 4, "y")
     _need(slot_pos, T * k * 4, "slot_pos")
     _need(topk_w, T * k * 4, "topk_w")
     _need(out, T * H * 4, "out")

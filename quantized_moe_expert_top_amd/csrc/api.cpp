@@ -157,7 +157,7 @@ size_t moe_w4a16_workspace(const moe_shape* s) {
 int moe_grouped_w4a16_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
                           const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
                           const int32_t* expert_offsets, const int32_t* sorted_slot,
-                          const int32_t* active, const int32_t* n_active, uint16_t* y, void* ws,
+                          const int32_t* active, const int32_t* n_active, float* y, void* ws,
                           size_t ws_bytes, void* stream) {
   int st = check_shape(s, MOE_GROUP, MOE_GROUP);
   if (st) return st;
@@ -190,7 +190,7 @@ size_t moe_w8a8_workspace(const moe_shape* s) {
 int moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int8_t* w13,
                          const float* s13, const int8_t* w2, const float* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
-                         const int32_t* active, const int32_t* n_active, uint16_t* y,
+                         const int32_t* active, const int32_t* n_active, float* y,
                          const moe_w8a8_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(s, 64, 64);
   if (st) return st;
@@ -222,7 +222,7 @@ int moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int8_t* w1
                   "moe_grouped_w8a8_ffn launch");
 }
 
-int moe_combine(const uint16_t* y, const int32_t* slot_pos, const float* topk_w, int32_t T,
+int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w, int32_t T,
                 int32_t H, int32_t k, float* out, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ESHAPE, "k = %d outside [1, %d]", k, MOE_MAX_TOPK);

@@ -9,7 +9,7 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int* __restrict__ slot_pos,
                                                       const float* __restrict__ w, int T, int H,
                                                       int k, float* __restrict__ out) {
@@ -22,15 +22,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int j = 0; j < k; ++j) {
     const float wj = w[static_cast<size_t>(t) * k + j];
     const int p = slot_pos[static_cast<size_t>(t) * k + j];
-    const uint4 v = ld16(y + static_cast<size_t>(p) * H + c * 8);
-    acc[0] += wj * bf16lo(v.x);
-    acc[1] += wj * bf16hi(v.x);
-    acc[2] += wj * bf16lo(v.y);
-    acc[3] += wj * bf16hi(v.y);
-    acc[4] += wj * bf16lo(v.z);
-    acc[5] += wj * bf16hi(v.z);
-    acc[6] += wj * bf16lo(v.w);
-    acc[7] += wj * bf16hi(v.w);
+    const float4* src = reinterpret_cast<const float4*>(y + static_cast<size_t>(p) * H + c * 8);
+    const float4 a = src[0], b = src[1];
+    acc[0] += wj * a.x;
+    acc[1] += wj * a.y;
+    acc[2] += wj * a.z;
+    acc[3] += wj * a.w;
+    acc[4] += wj * b.x;
+    acc[5] += wj * b.y;
+    acc[6] += wj * b.z;
+    acc[7] += wj * b.w;
   }
   float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * H + c * 8);
   o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* y, const int* slot_pos, const float* w, int T, int H,
+hipError_t launch_combine(const float* y, const int* slot_pos, const float* w, int T, int H,
                           int k, float* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const long long n = static_cast<long long>(T) * (H / 8);

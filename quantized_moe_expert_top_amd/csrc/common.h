@@ -55,7 +55,9 @@ __device__ __forceinline__ void nibble_pairs(uint32_t w, uint32_t& p0, uint32_t&
   p2 = ((w >> 8) & kMask) | kHi;
   p3 = ((w >> 12) & kMask) | kHi;
 }
-constexpr float kCodeBias = 136.0f;  // 128 (bf16 exponent trick) + 8 (zero point)
+// bf16 pair (136, 136): 128 (bf16 exponent trick) + 8 (zero point); the codes
+// of a zero weight widen to exactly this pattern.
+constexpr uint32_t kBiasPair = 0x43084308u;
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),

@@ -20,7 +20,7 @@ bool w4a16_uses_gemv(int T, int H, int I, int E, int k);
 hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                             const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
                             const uint16_t* s2, const int* offsets, const int* sorted_slot,
-                            const int* active, const int* n_active, uint16_t* y, void* ws,
+                            const int* active, const int* n_active, float* y, void* ws,
                             hipStream_t s);
 
 struct W8A8Debug {
@@ -35,10 +35,10 @@ size_t w8a8_workspace_bytes(int T, int H, int I, int E, int k);
 hipError_t launch_w8a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                            const int8_t* w13, const float* s13, const int8_t* w2,
                            const float* s2, const int* offsets, const int* sorted_slot,
-                           const int* active, const int* n_active, uint16_t* y,
+                           const int* active, const int* n_active, float* y,
                            const W8A8Debug& dbg, void* ws, hipStream_t s);
 
-hipError_t launch_combine(const uint16_t* y, const int* slot_pos, const float* w, int T, int H,
+hipError_t launch_combine(const float* y, const int* slot_pos, const float* w, int T, int H,
                           int k, float* out, hipStream_t s);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

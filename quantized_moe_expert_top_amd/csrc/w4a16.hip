@@ -9,13 +9,14 @@
 // section "Memory").
 //
 // Dequantization trick used by both kernels: a code q placed in the low
-// mantissa bits of bf16 0x4300 is exactly 128 + q. Dot products run on those
-// exact values; since the code is the same for the whole 128-wide group only
-// through its scale, the group's partial sum is
-//   sum_k x_k (q_k - 8) = sum_k x_k (128 + q_k) - 136 * sum_k x_k,
-// with the activation sums computed once when the activations are staged.
-// The scale is applied to the float32 partial sum of each group, so weights
-// are never rounded.
+// mantissa bits of bf16 0x4300 is exactly 128 + q, so widening a code costs
+// one mask-and-or per pair. Within one 128-wide group the scale is common, so
+//   sum_k x_k (q_k - 8) = sum_k x_k (128 + q_k) - sum_k x_k * 136,
+// and the scale multiplies the float32 difference once per group: weights
+// are never rounded. The bias term is computed by the very same instruction
+// chain with every code replaced by 8 (dot2 chain at staging for the GEMV, an
+// MFMA with constant B = 136 for the GEMM), so all-8 codes (a zero weight)
+// give exactly zero, and rounding in the two chains is correlated.
 //
 // Two kernels, chosen by batch size (a fixed rule, same tolerance for both):
 //  * decode (T <= 4): grouped GEMV. A block owns one routed expert and a strip
@@ -26,7 +27,7 @@
 //    registers and are widened right into the MFMA B operand; the gathered
 //    activation rows go through LDS.
 // Gate/up blocks pair gate row n with up row I + n in the same lane and apply
-// SwiGLU in the epilogue (h is stored bf16); down blocks write y (bf16).
+// SwiGLU in the epilogue (h is stored bf16); down blocks write y (float32).
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -39,13 +40,13 @@ constexpr int kGemvMaxT = 4;
 
 // ---------------------------------------------------------------- GEMV ----
 // KIND 0: gate/up (A = x rows of the expert's tokens, out = h [R, I]).
-// KIND 1: down    (A = h rows of the expert's block,  out = y [R, N]).
+// KIND 1: down    (A = h rows of the expert's block,  out = y float32 [R, N]).
 template <int KIND, int LK, int MAXM>
 __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const uint16_t* __restrict__ S, const int* __restrict__ offsets,
     const int* __restrict__ sorted_slot, const int* __restrict__ active,
-    const int* __restrict__ n_active, uint16_t* __restrict__ out, int K, int N, int topk,
+    const int* __restrict__ n_active, void* __restrict__ out, int K, int N, int topk,
     int tiles) {
   constexpr int G = kWave / LK;          // lane groups per wave
   constexpr int UB = (kThreads / kWave) * G;  // units per block
@@ -59,8 +60,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
   const int units = (KIND == 0) ? N / 2 : N / 2;
 
   extern __shared__ uint32_t lds[];
-  uint32_t* xs = lds;                                         // [MAXM][K/2]
-  float* csum = reinterpret_cast<float*>(lds + MAXM * (K / 2));  // [MAXM][C]
+  uint32_t* xs = lds;                                            // [MAXM][K/2]
+  float* bsum = reinterpret_cast<float*>(lds + MAXM * (K / 2));  // [MAXM][C]
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int g = lane / LK, lk = lane % LK;
@@ -77,23 +78,27 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 
   for (int m0 = 0; m0 < M; m0 += MAXM) {
     const int Mc = min(MAXM, M - m0);
-    // stage the rows: 32 values per (row, chunk), pair-permuted, plus sums
+    // stage the rows: 32 values per (row, chunk), pair-permuted, plus the
+    // chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the main
+    // loop (so all-8 codes cancel to an exact zero)
     for (int i = tid; i < Mc * C; i += kThreads) {
       const int m = i / C, c = i - m * C;
       const int p = p0 + m0 + m;
       const uint16_t* src = (KIND == 0)
           ? A + static_cast<size_t>(sorted_slot[p] / topk) * K + c * 32
           : A + static_cast<size_t>(p) * K + c * 32;
-      float sum = 0.0f;
+      float bias = 0.0f;
       uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint4 q = ld16(src + v * 8);
-        sum += bf16lo(q.x) + bf16hi(q.x) + bf16lo(q.y) + bf16hi(q.y) + bf16lo(q.z) +
-               bf16hi(q.z) + bf16lo(q.w) + bf16hi(q.w);
-        dst[v] = pair_permute(q);
+        const uint4 xv = pair_permute(ld16(src + v * 8));
+        bias = dot2_bf16(kBiasPair, xv.x, bias);
+        bias = dot2_bf16(kBiasPair, xv.y, bias);
+        bias = dot2_bf16(kBiasPair, xv.z, bias);
+        bias = dot2_bf16(kBiasPair, xv.w, bias);
+        dst[v] = xv;
       }
-      csum[m * C + c] = sum;
+      bsum[m * C + c] = bias;
     }
     __syncthreads();
 
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
           for (int m = 0; m < MAXM; ++m) {
             if (m < Mc) {
               const uint4* xp = reinterpret_cast<const uint4*>(xs + m * (K / 2) + c * 16);
-              const float cs = kCodeBias * csum[m * C + c];
+              const float cs = bsum[m * C + c];
               float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
@@ -161,9 +166,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
         if (m < Mc) {
           const size_t p = static_cast<size_t>(p0 + m0 + m);
           if (KIND == 0) {
-            out[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0[m], acc1[m]));
+            static_cast<uint16_t*>(out)[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0[m], acc1[m]));
           } else {
-            *reinterpret_cast<uint32_t*>(out + p * N + 2 * u) = pack_bf16x2(acc0[m], acc1[m]);
+            *reinterpret_cast<float2*>(static_cast<float*>(out) + p * N + 2 * u) =
+                make_float2(acc0[m], acc1[m]);
           }
         }
       }
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 template <int KIND, int LK, int MAXM>
 hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                          const int* offsets, const int* sorted_slot, const int* active,
-                         const int* n_active, uint16_t* out, int K, int N, int topk,
+                         const int* n_active, void* out, int K, int N, int topk,
                          int max_active, hipStream_t s) {
   constexpr int UB = (kThreads / kWave) * (kWave / LK);
   const int units = N / 2;
@@ -196,7 +202,7 @@ hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
 template <int KIND, int MAXM>
 hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                        const int* offsets, const int* sorted_slot, const int* active,
-                       const int* n_active, uint16_t* out, int K, int N, int topk,
+                       const int* n_active, void* out, int K, int N, int topk,
                        int max_active, hipStream_t s) {
   const int C = K / 32;
   if (C % 16 == 0 && C >= 64)
@@ -222,12 +228,11 @@ template <int KIND, int MT>
 __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const uint16_t* __restrict__ S, const int* __restrict__ offsets,
-    const int* __restrict__ sorted_slot, uint16_t* __restrict__ out, int K, int N, int E,
+    const int* __restrict__ sorted_slot, void* __restrict__ out, int K, int N, int E,
     int topk, int NT) {
   constexpr int BM = 32 * MT;
   constexpr int CPT = BM * 16 / kThreads;  // 16-byte A chunks per thread per group
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * kALd];
-  __shared__ __attribute__((aligned(16))) float c_lds[2][BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[3];
 
@@ -289,13 +294,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
     for (int v = 0; v < CPT; ++v) {
       const int q = tid + kThreads * v;
       const int r = q >> 4, ch = q & 15;
-      const uint4 x = regs[v];
-      float sum = bf16lo(x.x) + bf16hi(x.x) + bf16lo(x.y) + bf16hi(x.y) + bf16lo(x.z) +
-                  bf16hi(x.z) + bf16lo(x.w) + bf16hi(x.w);
-#pragma unroll
-      for (int sh = 8; sh >= 1; sh >>= 1) sum += wave_shfl_xor(sum, sh);
-      *reinterpret_cast<uint4*>(&a_lds[buf][r * kALd + ch * 8]) = pair_permute(x);
-      if (ch == 0) c_lds[buf][r] = kCodeBias * sum;
+      *reinterpret_cast<uint4*>(&a_lds[buf][r * kALd + ch * 8]) = pair_permute(regs[v]);
     }
   };
   auto load_b = [&](int g, uint4 (&bq)[2][2], float (&bs)[2]) {
@@ -330,13 +329,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
       load_a(g + 1, areg);
       load_b(g + 1, bq_next, bs_next);
     }
-    f32x16_t accg[MT][2];
+    // accg: the group's partial sums on 128 + q; cg: the same MFMA chain on
+    // constant 136 (= 128 + zero point), i.e. its exact bias term
+    f32x16_t accg[MT][2], cg[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cg[i][r] = 0.0f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) accg[i][j][r] = 0.0f;
+    }
+    const bf16x8_t bias_op = __builtin_bit_cast(
+        bf16x8_t, make_uint4(kBiasPair, kBiasPair, kBiasPair, kBiasPair));
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8_t bop[2];
@@ -355,22 +361,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[j], accg[i][j], 0, 0, 0);
+        cg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bias_op, cg[i], 0, 0, 0);
       }
     }
-    // scale and un-bias the group's partial sums
+    // un-bias and scale the group's partial sums
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float4 cb = *reinterpret_cast<const float4*>(&c_lds[buf][i * 32 + rb * 8 + hf * 4]);
-        const float cv[4] = {cb.x, cb.y, cb.z, cb.w};
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            acc[i][j][rb * 4 + r4] += bs[j] * (accg[i][j][rb * 4 + r4] - cv[r4]);
-      }
-    }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += bs[j] * (accg[i][j][r] - cg[i][r]);
     if (more) {
       store_a(buf ^ 1, areg);
 #pragma unroll
@@ -395,13 +395,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
       if (KIND == 0) {
         if (nvalid[0]) {
           const int n = ti.nt * 128 + wv * 32 + l32;
-          out[static_cast<size_t>(p) * (N / 2) + n] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+          static_cast<uint16_t*>(out)[static_cast<size_t>(p) * (N / 2) + n] =
+              f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           if (nvalid[j])
-            out[static_cast<size_t>(p) * N + nrow[j]] = f32_to_bf16(acc[i][j][r]);
+            static_cast<float*>(out)[static_cast<size_t>(p) * N + nrow[j]] = acc[i][j][r];
       }
     }
   }
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
 
 template <int KIND, int MT>
 hipError_t launch_mfma_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
-                         const int* offsets, const int* sorted_slot, uint16_t* out, int K, int N,
+                         const int* offsets, const int* sorted_slot, void* out, int K, int N,
                          int E, int topk, int T, hipStream_t s) {
   constexpr int BM = 32 * MT;
   const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + 255) / 256;
@@ -435,7 +436,7 @@ size_t w4a16_workspace_bytes(int T, int, int I, int, int k) {
 hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                             const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
                             const uint16_t* s2, const int* offsets, const int* sorted_slot,
-                            const int* active, const int* n_active, uint16_t* y, void* ws,
+                            const int* active, const int* n_active, float* y, void* ws,
                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   uint16_t* h = static_cast<uint16_t*>(ws);

@@ -10,7 +10,7 @@
 //   3. h_quant: the same per-row rule on h (one row per routed slot). h stays
 //      float32 until here so the code decisions match a float32 reference.
 //   4. down: int8 MFMA over (expert, 128-row, 128-column) tiles; y = acc *
-//      hs[p] * s2[e,n], stored bf16.
+//      hs[p] * s2[e,n], stored float32.
 // The int32 accumulators are exact, so they are reproducible bit for bit.
 #include "common.h"
 #include "launch.h"
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 //         [64wm, +64) and h-columns [32wn, +32): B subtile 0 = gate rows,
 //         subtile 1 = the matching up rows. Out: h float32 [R, I].
 // KIND 1: down. Tile = 128 rows x 128 W2 rows; wave (wm, wn) owns rows
-//         [64wm, +64) and W2 rows [64wn, +64) as two subtiles. Out: y bf16.
+//         [64wm, +64) and W2 rows [64wn, +64) as two subtiles. Out: y float32.
 // LDS holds the A tile (128 x 64 int8) and the B tile (128 W rows x 64 int8)
 // per pipeline step, double-buffered. Operand k order inside one MFMA step:
 // lane half hf = lane/32 takes k = 32*ks + 16*hf + [0, 16).
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const int8_t* __restrict__ W, const float* __restrict__ w_scale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_slot, int K, int N, int E,
-    int topk, int NT, float* __restrict__ h_out, uint16_t* __restrict__ y_out,
+    int topk, int NT, float* __restrict__ h_out, float* __restrict__ y_out,
     int32_t* __restrict__ dbg_acc) {
   __shared__ __attribute__((aligned(16))) int8_t a_lds[2][kBM * kLd];
   __shared__ __attribute__((aligned(16))) int8_t b_lds[2][kBM * kLd];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
           const int a = acc[i][j][r];
           if (dbg_acc) dbg_acc[static_cast<size_t>(p) * N + n] = a;
           y_out[static_cast<size_t>(p) * N + n] =
-              f32_to_bf16(static_cast<float>(a) * hsv * w_scale[static_cast<size_t>(ti.e) * N + n]);
+              static_cast<float>(a) * hsv * w_scale[static_cast<size_t>(ti.e) * N + n];
         }
       }
     }
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
 template <int KIND>
 hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t* W,
                             const float* w_scale, const int* offsets, const int* sorted_slot,
-                            int K, int N, int E, int topk, int T, float* h_out, uint16_t* y_out,
+                            int K, int N, int E, int topk, int T, float* h_out, float* y_out,
                             int32_t* dbg_acc, hipStream_t s) {
   const int NT = (KIND == 0) ? (N / 2 + 63) / 64 : (N + 127) / 128;
   const long long R = static_cast<long long>(T) * topk;
@@ -310,7 +310,7 @@ size_t w8a8_workspace_bytes(int T, int H, int I, int, int k) {
 hipError_t launch_w8a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                            const int8_t* w13, const float* s13, const int8_t* w2,
                            const float* s2, const int* offsets, const int* sorted_slot,
-                           const int*, const int*, uint16_t* y, const W8A8Debug& dbg, void* ws,
+                           const int*, const int*, float* y, const W8A8Debug& dbg, void* ws,
                            hipStream_t s) {
   if (T == 0) return hipSuccess;
   const W8A8Ws w = carve(ws, T, H, I, k);

@@ -94,7 +94,7 @@ def run_layer(wl, x_bits, logits, weights, debug=False):
         "slot_pos": to_np(b.slot_pos)[:R],
         "n_active": n_act,
         "active": to_np(b.active)[:n_act],
-        "y": bf16_np_to_f64(b.y)[:R] if R else np.zeros((0, wl.H)),
+        "y": to_np(b.y)[:R].astype(np.float64) if R else np.zeros((0, wl.H)),
         "out": to_np(b.out).astype(np.float64),
         "y_bits": to_np(b.y)[:R].copy(),
         "out_bits": to_np(b.out).view(np.uint32).copy(),

@@ -118,13 +118,13 @@ def test_combine_matches_oracle():
     import quantized_moe_expert_top_amd as moe
     rng = np.random.default_rng(1)
     T, H, k = 77, 520, 5
-    ybits = synth.bf16_bits_from_f32(rng.standard_normal((T * k, H)).astype(np.float32))
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
     slot_pos = rng.permutation(T * k).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    moe.combine(to_dev(ybits), to_dev(slot_pos), to_dev(w), out)
+    moe.combine(to_dev(y), to_dev(slot_pos), to_dev(w), out)
     torch.cuda.synchronize()
-    ref = oracle.combine(oracle.bf16_to_f64(ybits), slot_pos, w.astype(np.float64))
+    ref = oracle.combine(y.astype(np.float64), slot_pos, w.astype(np.float64))
     np.testing.assert_allclose(to_np(out), ref, rtol=1e-5, atol=1e-5)
 
 
