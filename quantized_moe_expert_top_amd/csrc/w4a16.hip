@@ -39,29 +39,50 @@ constexpr int kThreads = 256;
 constexpr int kGemvMaxT = 4;
 
 // ---------------------------------------------------------------- GEMV ----
-// KIND 0: gate/up (A = x rows of the expert's tokens, out = h [R, I]).
-// KIND 1: down    (A = h rows of the expert's block,  out = y float32 [R, N]).
-template <int KIND, int LK, int MAXM>
+// KIND 0: gate/up (A = x rows of the tokens, out = h bf16 [R, I]).
+// KIND 1: down    (A = h rows of the expert's block, out = y float32 [R, N]).
+// A block owns one routed expert (active slot blockIdx / tiles) and UB units
+// of output (a unit is a gate row with its up row, or two down rows). Inside
+// a wave, LK lanes split K: lane lk reads the 16-byte code chunks lk, lk+LK,
+// ... of each of its two rows (coalesced LK*16-byte runs), so per chunk the
+// 64 bytes of activations it needs are read from LDS once for both rows.
+//
+// Latency order: the expert id is the only thing the weight stream depends
+// on, so the first batch of code chunks is requested right after it. For the
+// gate/up kernel every token row of x is staged (decode has T <= 4), which
+// needs no routing information; which rows belong to the expert is looked up
+// while the weights are in flight. Loads are unconditional (indices clamped)
+// so they issue back to back; only the arithmetic is predicated.
+//
+// NB: code chunks per lane per batch (= chunks per lane when PIPE is false).
+// PIPE: more than NB chunks per lane; two register batches alternate.
+constexpr int kGemvMaxM = 4;
+
+template <int KIND, int LK, int NB, bool PIPE>
 __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const uint16_t* __restrict__ S, const int* __restrict__ offsets,
     const int* __restrict__ sorted_slot, const int* __restrict__ active,
     const int* __restrict__ n_active, void* __restrict__ out, int K, int N, int topk,
-    int tiles) {
-  constexpr int G = kWave / LK;          // lane groups per wave
+    int tiles, int T) {
+  constexpr int MAXM = kGemvMaxM;
+  constexpr int G = kWave / LK;               // lane groups per wave
   constexpr int UB = (kThreads / kWave) * G;  // units per block
   const int a = blockIdx.x / tiles;
-  if (a >= *n_active) return;
   const int tile = blockIdx.x - a * tiles;
-  const int e = active[a];
-  const int p0 = offsets[e];
-  const int M = offsets[e + 1] - p0;
-  const int C = K / 32;                  // 16-byte code chunks per row
-  const int units = (KIND == 0) ? N / 2 : N / 2;
+  const int na = *n_active;
+  const int e_raw = active[a];  // in bounds: grid has min(E, R) slots
+  if (a >= na) return;          // uniform per block, before any barrier
+  const int e = e_raw;
+  const int C = K / 32;         // 16-byte code chunks per row
+  const int nch = C / LK;       // chunks per lane (uniform)
+  const int units = N / 2;
 
   extern __shared__ uint32_t lds[];
-  uint32_t* xs = lds;                                            // [MAXM][K/2]
-  float* bsum = reinterpret_cast<float*>(lds + MAXM * (K / 2));  // [MAXM][C]
+  const int rows_staged = (KIND == 0) ? T : MAXM;
+  uint32_t* xs = lds;                                                  // [rows][K/2]
+  float* bsum = reinterpret_cast<float*>(lds + rows_staged * (K / 2));  // [rows][C]
+  __shared__ int tok[MAXM];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int g = lane / LK, lk = lane % LK;
@@ -71,148 +92,225 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
   const int r0 = (KIND == 0) ? uc : 2 * uc;
   const int r1 = (KIND == 0) ? N / 2 + uc : 2 * uc + 1;
   const size_t rowb = static_cast<size_t>(K / 2), rows = static_cast<size_t>(K / kGroup);
-  const uint8_t* W0 = W + (static_cast<size_t>(e) * N + r0) * rowb;
-  const uint8_t* W1 = W + (static_cast<size_t>(e) * N + r1) * rowb;
+  const uint8_t* W0 = W + (static_cast<size_t>(e) * N + r0) * rowb + lk * 16;
+  const uint8_t* W1 = W + (static_cast<size_t>(e) * N + r1) * rowb + lk * 16;
   const uint16_t* S0 = S + (static_cast<size_t>(e) * N + r0) * rows;
   const uint16_t* S1 = S + (static_cast<size_t>(e) * N + r1) * rows;
 
-  for (int m0 = 0; m0 < M; m0 += MAXM) {
-    const int Mc = min(MAXM, M - m0);
-    // stage the rows: 32 values per (row, chunk), pair-permuted, plus the
-    // chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the main
-    // loop (so all-8 codes cancel to an exact zero)
-    for (int i = tid; i < Mc * C; i += kThreads) {
+  uint4 qa0[NB], qa1[NB], qb0[NB], qb1[NB];
+  uint32_t sa[NB], sb[NB];  // raw fp16 scales: low half row 0, high half row 1
+  auto load_batch = [&](int i0, uint4 (&q0)[NB], uint4 (&q1)[NB], uint32_t (&sc)[NB]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = PIPE ? min(i0 + b, nch - 1) : b;
+      q0[b] = ld16(W0 + i * LK * 16);
+      q1[b] = ld16(W1 + i * LK * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = PIPE ? min(i0 + b, nch - 1) : b;
+      const int c = lk + i * LK;
+      sc[b] = static_cast<uint32_t>(S0[c >> 2]) | (static_cast<uint32_t>(S1[c >> 2]) << 16);
+    }
+  };
+  load_batch(0, qa0, qa1, sa);
+
+  const int p0 = offsets[e];
+  const int M = offsets[e + 1] - p0;
+
+  // stage activation rows: 32 values per (row, chunk), pair-permuted, plus the
+  // chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the main loop
+  // (so all-8 codes cancel to an exact zero)
+  auto stage = [&](int nrows, int m0) {
+    for (int i = tid; i < nrows * C; i += kThreads) {
       const int m = i / C, c = i - m * C;
-      const int p = p0 + m0 + m;
-      const uint16_t* src = (KIND == 0)
-          ? A + static_cast<size_t>(sorted_slot[p] / topk) * K + c * 32
-          : A + static_cast<size_t>(p) * K + c * 32;
+      const uint16_t* src = (KIND == 0) ? A + static_cast<size_t>(m) * K + c * 32
+                                        : A + static_cast<size_t>(p0 + m0 + m) * K + c * 32;
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xv[v] = ld16(src + v * 8);
       float bias = 0.0f;
       uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint4 xv = pair_permute(ld16(src + v * 8));
-        bias = dot2_bf16(kBiasPair, xv.x, bias);
-        bias = dot2_bf16(kBiasPair, xv.y, bias);
-        bias = dot2_bf16(kBiasPair, xv.z, bias);
-        bias = dot2_bf16(kBiasPair, xv.w, bias);
-        dst[v] = xv;
+        const uint4 p = pair_permute(xv[v]);
+        bias = dot2_bf16(kBiasPair, p.x, bias);
+        bias = dot2_bf16(kBiasPair, p.y, bias);
+        bias = dot2_bf16(kBiasPair, p.z, bias);
+        bias = dot2_bf16(kBiasPair, p.w, bias);
+        dst[v] = p;
       }
       bsum[m * C + c] = bias;
     }
-    __syncthreads();
+  };
+  if (KIND == 0) stage(T, 0);
 
-    float acc0[MAXM], acc1[MAXM];
+  // one 16-byte chunk (32 codes) of both rows against one staged activation row
+  auto dot_chunk = [&](const uint4& q0, const uint4& q1, int xr, int c, float& d0, float& d1) {
+    const uint4* xp = reinterpret_cast<const uint4*>(xs + xr * (K / 2) + c * 16);
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) acc0[m] = acc1[m] = 0.0f;
-
-    for (int cb = lk; cb < C; cb += 4 * LK) {
-      uint4 q0[4], q1[4];
-      float s0[4], s1[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c = cb + b * LK;
-        if (c < C) {
-          q0[b] = ld16(W0 + c * 16);
-          q1[b] = ld16(W1 + c * 16);
-          s0[b] = fp16_bits_to_f32(S0[c >> 2]);
-          s1[b] = fp16_bits_to_f32(S1[c >> 2]);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c = cb + b * LK;
-        if (c < C) {
-#pragma unroll
-          for (int m = 0; m < MAXM; ++m) {
-            if (m < Mc) {
-              const uint4* xp = reinterpret_cast<const uint4*>(xs + m * (K / 2) + c * 16);
-              const float cs = bsum[m * C + c];
-              float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const uint4 xv = xp[v];
-                const uint32_t w0 = (&q0[b].x)[v], w1 = (&q1[b].x)[v];
-                uint32_t a0, a1, a2, a3;
-                nibble_pairs(w0, a0, a1, a2, a3);
-                d0 = dot2_bf16(a0, xv.x, d0);
-                d0 = dot2_bf16(a1, xv.y, d0);
-                d0 = dot2_bf16(a2, xv.z, d0);
-                d0 = dot2_bf16(a3, xv.w, d0);
-                nibble_pairs(w1, a0, a1, a2, a3);
-                d1 = dot2_bf16(a0, xv.x, d1);
-                d1 = dot2_bf16(a1, xv.y, d1);
-                d1 = dot2_bf16(a2, xv.z, d1);
-                d1 = dot2_bf16(a3, xv.w, d1);
-              }
-              acc0[m] += s0[b] * (d0 - cs);
-              acc1[m] += s1[b] * (d1 - cs);
-            }
-          }
-        }
-      }
+    for (int v = 0; v < 4; ++v) {
+      const uint4 xv = xp[v];
+      uint32_t w0 = (&q0.x)[v], w1 = (&q1.x)[v];
+      // keep the widening inside the row loop: hoisting it would hold 4x the
+      // code registers live for every row pass, and most experts see one row
+      asm volatile("" : "+v"(w0), "+v"(w1));
+      uint32_t a0, a1, a2, a3;
+      nibble_pairs(w0, a0, a1, a2, a3);
+      d0 = dot2_bf16(a0, xv.x, d0);
+      d0 = dot2_bf16(a1, xv.y, d0);
+      d0 = dot2_bf16(a2, xv.z, d0);
+      d0 = dot2_bf16(a3, xv.w, d0);
+      nibble_pairs(w1, a0, a1, a2, a3);
+      d1 = dot2_bf16(a0, xv.x, d1);
+      d1 = dot2_bf16(a1, xv.y, d1);
+      d1 = dot2_bf16(a2, xv.z, d1);
+      d1 = dot2_bf16(a3, xv.w, d1);
     }
+  };
+  auto finish = [&](float acc0, float acc1, int m) {
 #pragma unroll
     for (int sh = LK / 2; sh >= 1; sh >>= 1) {
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        acc0[m] += wave_shfl_xor(acc0[m], sh);
-        acc1[m] += wave_shfl_xor(acc1[m], sh);
-      }
+      acc0 += wave_shfl_xor(acc0, sh);
+      acc1 += wave_shfl_xor(acc1, sh);
     }
     if (lk == 0 && valid) {
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        if (m < Mc) {
-          const size_t p = static_cast<size_t>(p0 + m0 + m);
-          if (KIND == 0) {
-            static_cast<uint16_t*>(out)[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0[m], acc1[m]));
-          } else {
-            *reinterpret_cast<float2*>(static_cast<float*>(out) + p * N + 2 * u) =
-                make_float2(acc0[m], acc1[m]);
-          }
-        }
+      const size_t p = static_cast<size_t>(p0 + m);
+      if (KIND == 0) {
+        static_cast<uint16_t*>(out)[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0, acc1));
+      } else {
+        *reinterpret_cast<float2*>(static_cast<float*>(out) + p * N + 2 * u) =
+            make_float2(acc0, acc1);
       }
     }
-    __syncthreads();  // LDS is restaged by the next row chunk
+  };
+
+  // rows are taken in chunks of MAXM (normally one chunk: M <= T <= 4)
+  for (int m0 = 0; m0 < M; m0 += MAXM) {
+    const int Mc = min(MAXM, M - m0);
+    if (KIND == 0) {
+      if (tid < Mc) tok[tid] = sorted_slot[p0 + m0 + tid] / topk;
+    } else {
+      stage(Mc, m0);
+    }
+    __syncthreads();
+    if (!PIPE) {
+      // all of this lane's codes are in registers: one pass per row
+      for (int m = 0; m < Mc; ++m) {
+        const int xr = (KIND == 0) ? tok[m] : m;
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int c = lk + b * LK;
+          float d0 = 0.0f, d1 = 0.0f;
+          dot_chunk(qa0[b], qa1[b], xr, c, d0, d1);
+          const float cs = bsum[xr * C + c];
+          acc0 += fp16_bits_to_f32(static_cast<uint16_t>(sa[b] & 0xFFFFu)) * (d0 - cs);
+          acc1 += fp16_bits_to_f32(static_cast<uint16_t>(sa[b] >> 16)) * (d1 - cs);
+        }
+        finish(acc0, acc1, m0 + m);
+      }
+    } else {
+      // codes stream through two register batches; rows two at a time
+      for (int mp = 0; mp < Mc; mp += 2) {
+        const bool two = mp + 1 < Mc;
+        const int xr0 = (KIND == 0) ? tok[mp] : mp;
+        const int xr1 = two ? ((KIND == 0) ? tok[mp + 1] : mp + 1) : xr0;
+        float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+        auto compute_batch = [&](int i0, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
+                                 const uint32_t (&sc)[NB]) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            if (i0 + b < nch) {
+              const int c = lk + (i0 + b) * LK;
+              const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu));
+              const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16));
+              float d0 = 0.0f, d1 = 0.0f;
+              dot_chunk(q0[b], q1[b], xr0, c, d0, d1);
+              const float cs0 = bsum[xr0 * C + c];
+              acc[0][0] += s0 * (d0 - cs0);
+              acc[0][1] += s1 * (d1 - cs0);
+              if (two) {
+                float e0 = 0.0f, e1 = 0.0f;
+                dot_chunk(q0[b], q1[b], xr1, c, e0, e1);
+                const float cs1 = bsum[xr1 * C + c];
+                acc[1][0] += s0 * (e0 - cs1);
+                acc[1][1] += s1 * (e1 - cs1);
+              }
+            }
+          }
+        };
+        if (m0 != 0 || mp != 0) load_batch(0, qa0, qa1, sa);   // first pass reuses the prefetch
+        for (int i0 = 0; i0 < nch; i0 += 2 * NB) {
+          if (i0 + NB < nch) load_batch(i0 + NB, qb0, qb1, sb);
+          compute_batch(i0, qa0, qa1, sa);
+          if (i0 + 2 * NB < nch) load_batch(i0 + 2 * NB, qa0, qa1, sa);
+          if (i0 + NB < nch) compute_batch(i0 + NB, qb0, qb1, sb);
+        }
+        finish(acc[0][0], acc[0][1], m0 + mp);
+        if (two) finish(acc[1][0], acc[1][1], m0 + mp + 1);
+      }
+    }
+    __syncthreads();  // tok / LDS rows are rewritten by the next row chunk
   }
 }
 
-template <int KIND, int LK, int MAXM>
+template <int KIND, int LK, int NB, bool PIPE>
 hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                          const int* offsets, const int* sorted_slot, const int* active,
                          const int* n_active, void* out, int K, int N, int topk,
-                         int max_active, hipStream_t s) {
+                         int max_active, int T, hipStream_t s) {
   constexpr int UB = (kThreads / kWave) * (kWave / LK);
   const int units = N / 2;
   const int tiles = (units + UB - 1) / UB;
-  const size_t lds = static_cast<size_t>(MAXM) * (K / 2) * 4 + static_cast<size_t>(MAXM) * (K / 32) * 4;
+  const int rows_staged = (KIND == 0) ? T : kGemvMaxM;
+  const size_t lds = static_cast<size_t>(rows_staged) * (K / 2) * 4 +
+                     static_cast<size_t>(rows_staged) * (K / 32) * 4;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a16_gemv_kernel<KIND, LK, MAXM>),
+        reinterpret_cast<const void*>(&w4a16_gemv_kernel<KIND, LK, NB, PIPE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, LK, MAXM>), dim3(max_active * tiles),
+  hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, LK, NB, PIPE>), dim3(max_active * tiles),
                      dim3(kThreads), lds, s, A, W, S, offsets, sorted_slot, active, n_active,
-                     out, K, N, topk, tiles);
+                     out, K, N, topk, tiles, T);
   return hipGetLastError();
 }
 
-template <int KIND, int MAXM>
+template <int KIND, int LK>
+hipError_t launch_gemv_lk(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                          const int* offsets, const int* sorted_slot, const int* active,
+                          const int* n_active, void* out, int K, int N, int topk,
+                          int max_active, int T, hipStream_t s) {
+  const int nch = K / 32 / LK;
+#define MOE_GEMV_CASE(NB_, PIPE_)                                                              \
+  return launch_gemv_t<KIND, LK, NB_, PIPE_>(A, W, S, offsets, sorted_slot, active, n_active, \
+                                             out, K, N, topk, max_active, T, s)
+  switch (nch) {
+    case 1: MOE_GEMV_CASE(1, false);
+    case 2: MOE_GEMV_CASE(2, false);
+    case 3: MOE_GEMV_CASE(3, false);
+    case 4: MOE_GEMV_CASE(4, false);
+    default: MOE_GEMV_CASE(4, true);
+  }
+#undef MOE_GEMV_CASE
+}
+
+template <int KIND>
 hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                        const int* offsets, const int* sorted_slot, const int* active,
                        const int* n_active, void* out, int K, int N, int topk,
-                       int max_active, hipStream_t s) {
+                       int max_active, int T, hipStream_t s) {
   const int C = K / 32;
   if (C % 16 == 0 && C >= 64)
-    return launch_gemv_t<KIND, 16, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out,
-                                         K, N, topk, max_active, s);
+    return launch_gemv_lk<KIND, 16>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
+                                    topk, max_active, T, s);
   if (C % 8 == 0)
-    return launch_gemv_t<KIND, 8, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out,
-                                        K, N, topk, max_active, s);
-  return launch_gemv_t<KIND, 4, MAXM>(A, W, S, offsets, sorted_slot, active, n_active, out, K,
-                                      N, topk, max_active, s);
+    return launch_gemv_lk<KIND, 8>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
+                                   topk, max_active, T, s);
+  return launch_gemv_lk<KIND, 4>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
+                                 topk, max_active, T, s);
 }
 
 // ---------------------------------------------------------------- MFMA ----
@@ -444,18 +542,11 @@ hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x
   const int max_active = R < E ? R : E;
   hipError_t err;
   if (T <= kGemvMaxT) {
-    if (T <= 2) {
-      err = launch_gemv<0, 2>(x, w13, s13, offsets, sorted_slot, active, n_active, h, H, 2 * I, k,
-                              max_active, s);
-      if (err != hipSuccess) return err;
-      return launch_gemv<1, 2>(h, w2, s2, offsets, sorted_slot, active, n_active, y, I, H, k,
-                               max_active, s);
-    }
-    err = launch_gemv<0, 4>(x, w13, s13, offsets, sorted_slot, active, n_active, h, H, 2 * I, k,
-                            max_active, s);
+    err = launch_gemv<0>(x, w13, s13, offsets, sorted_slot, active, n_active, h, H, 2 * I, k,
+                         max_active, T, s);
     if (err != hipSuccess) return err;
-    return launch_gemv<1, 4>(h, w2, s2, offsets, sorted_slot, active, n_active, y, I, H, k,
-                             max_active, s);
+    return launch_gemv<1>(h, w2, s2, offsets, sorted_slot, active, n_active, y, I, H, k,
+                          max_active, T, s);
   }
   const double avg_rows = static_cast<double>(R) / max_active;
   if (avg_rows <= 48.0) {
