@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="decode_t2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of HIP graphs")
+    ap.add_argument("--path", choices=("layer", "calls"), default=None,
+                    help="layer: moe_layer_w4a16 (one call per layer; W4A16 only); "
+                         "calls: the four separate calls. Default: layer for W4A16")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     return ap.parse_args()
 
@@ -102,9 +105,16 @@ def main():
         ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active, b.n_active, b.y,
             b.ffn_ws)
 
+    path = args.path or ("layer" if wl.fmt == "w4a16" else "calls")
+    if path == "layer" and wl.fmt != "w4a16":
+        raise SystemExit("--path layer covers W4A16 workloads")
+
     def layer(u):
-        x, L, _ = units[u]
+        x, L, wts = units[u]
         b = bufs[u]
+        if path == "layer":
+            moe.moe_layer(b, x, L, wts)
+            return
         moe.route_topk(L, wl.k, b.ids, b.w)
         moe.permute(b.ids, wl.E, b.offsets, b.sorted_slot, b.slot_pos, b.active, b.n_active,
                     b.perm_ws)
@@ -127,11 +137,12 @@ def main():
                 for u in us:
                     layer(u)
             step_graphs.append(g)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for u in us:
-                    ffn_call(u)
-            ffn_graphs.append(g)
+            if path == "calls":
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for u in us:
+                        ffn_call(u)
+                ffn_graphs.append(g)
 
     def run_step(i):
         if args.eager:
@@ -150,7 +161,8 @@ def main():
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         run_step(i)
-        run_ffn(i)
+        if path == "calls":
+            run_ffn(i)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps of the whole path
@@ -168,19 +180,27 @@ def main():
     ms_per_step = ms_total / args.steps
     value = wl.T * args.steps / (ms_total / 1e3)   # each step carries T tokens
 
-    # dominant kernel: the grouped FFN calls of the same K steps, back to back
-    # on the same stream, timed with HIP events
-    f0 = torch.cuda.Event(enable_timing=True)
-    f1 = torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for i in range(args.steps):
-        run_ffn(i)
-    f1.record(stream)
-    torch.cuda.synchronize()
     calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
-    avg_ms = f0.elapsed_time(f1) / len(calls)
     eb = expert_bytes(wl)
-    io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 4   # x in (bf16), y out (float32)
+    if path == "layer":
+        # dominant unit: the whole-layer call (its kernels carry all of the
+        # layer's bytes); per-call time from the timed region itself
+        avg_ms = ms_total / len(calls)
+        io_bytes = wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 4  # x, logits, out
+        kernel = "moe_layer_w4a16 (whole layer: decode_gateup_kernel + decode_down_kernel at T <= 4)"
+    else:
+        # dominant kernel: the grouped FFN calls of the same K steps, back to
+        # back on the same stream, timed with HIP events
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for i in range(args.steps):
+            run_ffn(i)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        avg_ms = f0.elapsed_time(f1) / len(calls)
+        io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 4   # x in (bf16), y out (float32)
+        kernel = f"moe_grouped_{wl.fmt}_ffn (gate/up + down kernels)"
     avg_bytes = sum(act_per_unit[u] * eb + io_bytes for u in calls) / len(calls)
     achieved = avg_bytes / (avg_ms / 1e3) / 1e9
     flops_per_call = 6.0 * wl.H * wl.I * wl.T * wl.k
@@ -191,7 +211,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": None,
-        "kernel": f"moe_grouped_{wl.fmt}_ffn (gate/up + down kernels)",
+        "kernel": kernel,
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "algo_bytes_per_launch": int(avg_bytes),
     }
@@ -217,6 +237,7 @@ def main():
                    "format": "W4A16 g128" if wl.fmt == "w4a16" else "W8A8",
                    "layers_per_step": len(schedule[0]),
                    "launch": "eager" if args.eager else "hip_graph_per_step",
+                   "path": path,
                    "mean_active_experts": round(float(np.mean(list(act_per_unit.values()))), 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -150,6 +150,33 @@ MOE_API int moe_grouped_w4a16_ffn(const moe_shape* shape, const uint16_t* x,
                           const int32_t* active, const int32_t* n_active,
                           float* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_layer_w4a16 — the whole W4A16 layer in one call, with the outputs of
+ * moe_route_topk (topk_ids, topk_w), moe_permute (expert_offsets,
+ * sorted_slot, slot_pos, active, n_active), moe_grouped_w4a16_ffn (y) and
+ * moe_combine (out), computed by the same definitions. [PV-fast] (one graph
+ * per decode step, no host synchronization inside) [MS] (no per-layer host
+ * probe)
+ * For T <= 4 (decode) it runs two kernels instead of the five launches of the
+ * separate calls: every block of the first routes all T tokens itself,
+ * rebuilds the permutation in LDS and runs its gate/up tile (block 0 writes
+ * the routing outputs); the second runs the down tiles and the combine, whose
+ * k-ordered sum for a (token, row tile) is taken by whichever block completes
+ * that token's k rows last (an integer counter decides; the order of the sum
+ * is fixed, so results are bitwise those of moe_combine's order).
+ * For larger T it enqueues the four steps. `logits` float32 [T, E]; other
+ * arguments as in the individual calls. Requires H % 128 == 0, I % 128 == 0.
+ * `ws` must hold moe_layer_w4a16_workspace(shape) bytes.
+ */
+MOE_API size_t moe_layer_w4a16_workspace(const moe_shape* shape);
+MOE_API int moe_layer_w4a16(const moe_shape* shape, const float* logits, const uint16_t* x,
+                            const uint8_t* w13, const uint16_t* s13,
+                            const uint8_t* w2, const uint16_t* s2,
+                            int32_t* topk_ids, float* topk_w,
+                            int32_t* expert_offsets, int32_t* sorted_slot,
+                            int32_t* slot_pos, int32_t* active, int32_t* n_active,
+                            float* y, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Optional W8A8 intermediate outputs (device pointers; any may be NULL). */
 typedef struct {
   int8_t* xq;     /* [T, H]   per-token int8 activations                 */

@@ -10,12 +10,12 @@ from dataclasses import dataclass
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    MoeError, combine, grouped_w4a16_ffn, grouped_w8a8_ffn, load, permute,
-    permute_workspace, route_topk, w4a16_workspace, w8a8_workspace,
+    MoeError, combine, grouped_w4a16_ffn, grouped_w8a8_ffn, layer_w4a16, layer_w4a16_workspace,
+    load, permute, permute_workspace, route_topk, w4a16_workspace, w8a8_workspace,
 )
 
-__all__ = ["MoeError", "LayerBuffers", "moe_forward", "load", "route_topk", "permute",
-           "grouped_w4a16_ffn", "grouped_w8a8_ffn", "combine"]
+__all__ = ["MoeError", "LayerBuffers", "moe_forward", "moe_layer", "load", "route_topk",
+           "permute", "grouped_w4a16_ffn", "grouped_w8a8_ffn", "combine", "layer_w4a16"]
 
 
 @dataclass
@@ -36,6 +36,7 @@ class LayerBuffers:
     n_active: object
     perm_ws: object
     ffn_ws: object
+    layer_ws: object
     y: object
     out: object
 
@@ -46,6 +47,7 @@ class LayerBuffers:
         i32 = dict(dtype=torch.int32, device=device)
         pws = _lib.permute_workspace(T, E, k)
         fws = (_lib.w4a16_workspace if fmt == "w4a16" else _lib.w8a8_workspace)(T, H, I, E, k)
+        lws = _lib.layer_w4a16_workspace(T, H, I, E, k) if fmt == "w4a16" else 0
         return cls(
             T, H, I, E, k, fmt,
             ids=torch.empty((T, k), **i32),
@@ -57,6 +59,7 @@ class LayerBuffers:
             n_active=torch.empty(4, **i32),
             perm_ws=torch.empty(max(pws, 16), dtype=torch.uint8, device=device),
             ffn_ws=torch.empty(max(fws, 16), dtype=torch.uint8, device=device),
+            layer_ws=torch.empty(max(lws, 16), dtype=torch.uint8, device=device),
             y=torch.empty((max(R, 1), H), dtype=torch.float32, device=device),
             out=torch.empty((T, H), dtype=torch.float32, device=device),
         )
@@ -77,4 +80,16 @@ def moe_forward(b: LayerBuffers, x, logits, weights, debug=None, stream=None):
         _lib.grouped_w8a8_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
                               b.n_active, b.y, b.ffn_ws, debug, stream)
     _lib.combine(b.y, b.slot_pos, b.w, b.out, stream)
+    return b.out
+
+
+def moe_layer(b: LayerBuffers, x, logits, weights, stream=None):
+    """The same layer through the single whole-layer entry point
+    (moe_layer_w4a16; fused kernels at decode sizes). Returns b.out."""
+    if b.fmt != "w4a16":
+        raise ValueError("moe_layer covers the W4A16 format")
+    w13, s13, w2, s2 = weights
+    _lib.layer_w4a16((b.T, b.H, b.I, b.E, b.k), logits, x, w13, s13, w2, s2, b.ids, b.w,
+                     b.offsets, b.sorted_slot, b.slot_pos, b.active, b.n_active, b.y, b.out,
+                     b.layer_ws, stream)
     return b.out

@@ -19,7 +19,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN",
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_route_topk",
            "moe_permute_workspace", "moe_permute", "moe_w4a16_workspace",
            "moe_grouped_w4a16_ffn", "moe_w8a8_workspace", "moe_grouped_w8a8_ffn",
-           "moe_combine")
+           "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_w8a8_ffn": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 10 +
                                  [ctypes.POINTER(MoeW8A8Debug), P, SZ, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
+        "moe_layer_w4a16_workspace": (SZ, [ctypes.POINTER(MoeShape)]),
+        "moe_layer_w4a16": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 16 + [SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -221,3 +223,31 @@ def combine(y, slot_pos, topk_w, out, stream=None) -> None:
     _need(out, T * H * 4, "out")
     _check("moe_combine", load().moe_combine(_ptr(y), _ptr(slot_pos), _ptr(topk_w), T, H, k,
                                              _ptr(out), _stream(stream)))
+
+
+def layer_w4a16_workspace(T: int, H: int, I: int, E: int, k: int) -> int:
+    s = MoeShape(T, H, I, E, k)
+    return int(load().moe_layer_w4a16_workspace(ctypes.byref(s)))
+
+
+def layer_w4a16(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                sorted_slot, slot_pos, active, n_active, y, out, ws, stream=None) -> None:
+    T, H, I, E, k = shape
+    R = T * k
+    if T > 0 and H % 128 == 0 and I % 128 == 0:
+        _check_ffn_sizes(shape, x, expert_offsets, sorted_slot, active, n_active, y)
+        _need(logits, T * E * 4, "logits")
+        _need(w13, E * 2 * I * H // 2, "w13")
+        _need(s13, E * 2 * I * (H // 128) * 2, "s13")
+        _need(w2, E * H * I // 2, "w2")
+        _need(s2, E * H * (I // 128) * 2, "s2")
+        _need(topk_ids, R * 4, "topk_ids")
+        _need(topk_w, R * 4, "topk_w")
+        _need(slot_pos, R * 4, "slot_pos")
+        _need(out, T * H * 4, "out")
+    s = MoeShape(*shape)
+    nbytes = ws.numel() * ws.element_size()
+    _check("moe_layer_w4a16", load().moe_layer_w4a16(
+        ctypes.byref(s), _ptr(logits), _ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_slot), _ptr(slot_pos),
+        _ptr(active), _ptr(n_active), _ptr(y), _ptr(out), _ptr(ws), nbytes, _stream(stream)))

@@ -182,6 +182,47 @@ int moe_grouped_w4a16_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* 
                   "moe_grouped_w4a16_ffn launch");
 }
 
+size_t moe_layer_w4a16_workspace(const moe_shape* s) {
+  if (check_shape(s, MOE_GROUP, MOE_GROUP)) return 0;
+  return moe::w4a16_layer_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
+}
+
+int moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16_t* x,
+                    const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
+                    const uint16_t* s2, int32_t* topk_ids, float* topk_w,
+                    int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                    int32_t* active, int32_t* n_active, float* y, float* out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  if (st) return st;
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(n_active);
+  const size_t need = moe::w4a16_layer_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "layer workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE_PTR(ws);
+  if (s->T > 0) {
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(s13);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(s2);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(sorted_slot);
+    REQUIRE_PTR(slot_pos);
+    REQUIRE_PTR(active);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(out);
+  }
+  if ((st = check_device())) return st;
+  return launched(moe::launch_w4a16_layer(s->T, s->H, s->I, s->E, s->k, logits, x, w13, s13, w2,
+                                          s2, topk_ids, topk_w, expert_offsets, sorted_slot,
+                                          slot_pos, active, n_active, y, out, ws,
+                                          static_cast<hipStream_t>(stream)),
+                  "moe_layer_w4a16 launch");
+}
+
 size_t moe_w8a8_workspace(const moe_shape* s) {
   if (check_shape(s, 64, 64)) return 0;
   return moe::w8a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);

@@ -73,10 +73,120 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
-// Non-temporal-free 16-byte global load (plain; the compiler emits
-// global_load_dwordx4).
+// Top-k routing of one token by one wavefront ("Performance and verification",
+// section "How it is verified": router ids are exact integer outputs).
+// Each lane holds E/64 logits as 64-bit keys
+//   key = orderable(logit) << 32 | (0xFFFFFFFF - expert)
+// so the unsigned maximum is the largest logit with the lowest expert index on
+// ties (+0.0 and -0.0 are made equal first). k rounds of a wave-wide max pick
+// the experts in descending order; the owner lane clears the winner's key.
+// The weights are a float32 softmax over the k selected logits. Lane j < k
+// writes pick j to ids[j], w[j] (generic pointers: global memory or LDS).
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  uint32_t b = __float_as_uint(l);
+  if (b == 0x80000000u) b = 0u;  // -0.0 ties +0.0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+
+// Wave-wide max / sum through DPP (row_shr 1,2,4,8 inside 16-lane rows, then
+// row_bcast 15/31 across rows) and a read of lane 63: a few cycles per step
+// instead of an LDS permute per step. All 64 lanes must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, true)));
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, true)));
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, true)));
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, true)));
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, BOUND));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0x111, 0xf, true>(v);
+  v += dpp_f32<0x112, 0xf, true>(v);
+  v += dpp_f32<0x114, 0xf, true>(v);
+  v += dpp_f32<0x118, 0xf, true>(v);
+  v += dpp_f32<0x142, 0xa, false>(v);
+  v += dpp_f32<0x143, 0xc, false>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int S>  // key slots per lane: E <= 64 * S
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int* ids,
+                                          float* w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t key[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = lane + kWave * s;
+    key[s] = (e < E) ? route_key(row[e], e) : 0ull;  // valid keys are > 0
+  }
+  int my_e = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) best = key[s] > best ? key[s] : best;
+    // the 64-bit wave max as two 32-bit ones: the largest logit, then the
+    // lowest expert index among the lanes holding it
+    const uint32_t hi = static_cast<uint32_t>(best >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? static_cast<uint32_t>(best) : 0u);
+    const uint64_t win = (static_cast<uint64_t>(mh) << 32) | ml;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (key[s] == win) key[s] = 0ull;
+    const int e = static_cast<int>(0xFFFFFFFFu - ml);
+    if (lane == j) {
+      my_e = e;
+      my_l = row[e];
+    }
+  }
+  // softmax over the k picks; pick 0 holds the maximum
+  const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+  const float z = (lane < k) ? expf(my_l - lmax) : 0.0f;
+  const float sum = wave_sum_f32(z);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = z / sum;
+  }
+}
+
+// 16-byte global load (global_load_dwordx4).
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+
+// Block-wide exclusive scan of one int per thread for 256-thread blocks;
+// `wave_tot` is a 4-int LDS scratch. Contains two barriers: call it from all
+// threads of the block.
+__device__ __forceinline__ int block256_excl_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = wave_tot[i];
+    if (i < w) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - v;
 }
 
 }  // namespace moe

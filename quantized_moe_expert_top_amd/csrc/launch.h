@@ -23,6 +23,14 @@ hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x
                             const int* active, const int* n_active, float* y, void* ws,
                             hipStream_t s);
 
+// Whole layer (route, permute, grouped FFN, combine); small T runs fused kernels.
+size_t w4a16_layer_workspace_bytes(int T, int H, int I, int E, int k);
+hipError_t launch_w4a16_layer(int T, int H, int I, int E, int k, const float* logits,
+                              const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                              const uint8_t* w2, const uint16_t* s2, int* ids, float* w,
+                              int* offsets, int* sorted_slot, int* slot_pos, int* active,
+                              int* n_active, float* y, float* out, void* ws, hipStream_t s);
+
 struct W8A8Debug {
   int8_t* xq;
   float* xs;

@@ -41,11 +41,11 @@ constexpr int kGemvMaxT = 4;
 // ---------------------------------------------------------------- GEMV ----
 // KIND 0: gate/up (A = x rows of the tokens, out = h bf16 [R, I]).
 // KIND 1: down    (A = h rows of the expert's block, out = y float32 [R, N]).
-// A block owns one routed expert (active slot blockIdx / tiles) and UB units
-// of output (a unit is a gate row with its up row, or two down rows). Inside
-// a wave, LK lanes split K: lane lk reads the 16-byte code chunks lk, lk+LK,
-// ... of each of its two rows (coalesced LK*16-byte runs), so per chunk the
-// 64 bytes of activations it needs are read from LDS once for both rows.
+// A block owns one routed expert and UB units of output (a unit is a gate row
+// with its up row, or two down rows). Inside a wave, LK lanes split K: lane
+// lk reads the 16-byte code chunks lk, lk+LK, ... of each of its two rows
+// (coalesced LK*16-byte runs), so per chunk the 64 bytes of activations it
+// needs are read from LDS once for both rows.
 //
 // Latency order: the expert id is the only thing the weight stream depends
 // on, so the first batch of code chunks is requested right after it. For the
@@ -58,31 +58,74 @@ constexpr int kGemvMaxT = 4;
 // PIPE: more than NB chunks per lane; two register batches alternate.
 constexpr int kGemvMaxM = 4;
 
-template <int KIND, int LK, int NB, bool PIPE>
-__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
-    const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
-    const uint16_t* __restrict__ S, const int* __restrict__ offsets,
-    const int* __restrict__ sorted_slot, const int* __restrict__ active,
-    const int* __restrict__ n_active, void* __restrict__ out, int K, int N, int topk,
-    int tiles, int T) {
-  constexpr int MAXM = kGemvMaxM;
-  constexpr int G = kWave / LK;               // lane groups per wave
-  constexpr int UB = (kThreads / kWave) * G;  // units per block
-  const int a = blockIdx.x / tiles;
-  const int tile = blockIdx.x - a * tiles;
-  const int na = *n_active;
-  const int e_raw = active[a];  // in bounds: grid has min(E, R) slots
-  if (a >= na) return;          // uniform per block, before any barrier
-  const int e = e_raw;
-  const int C = K / 32;         // 16-byte code chunks per row
-  const int nch = C / LK;       // chunks per lane (uniform)
-  const int units = N / 2;
+template <int KIND, int LK>
+struct GemvGeom {
+  static constexpr int G = kWave / LK;               // lane groups per wave
+  static constexpr int UB = (kThreads / kWave) * G;  // units per block
+};
 
-  extern __shared__ uint32_t lds[];
-  const int rows_staged = (KIND == 0) ? T : MAXM;
-  uint32_t* xs = lds;                                                  // [rows][K/2]
-  float* bsum = reinterpret_cast<float*>(lds + rows_staged * (K / 2));  // [rows][C]
-  __shared__ int tok[MAXM];
+// Stage activation rows into LDS: 32 values per (row, chunk), pair-permuted,
+// plus each chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the
+// main loop (so all-8 codes cancel to an exact zero). Row m comes from
+// src + m * K.
+__device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int nrows, int K,
+                                           uint32_t* xs, float* bsum) {
+  const int C = K / 32;
+  for (int i = threadIdx.x; i < nrows * C; i += kThreads) {
+    const int m = i / C, c = i - m * C;
+    const uint16_t* p = src + static_cast<size_t>(m) * K + c * 32;
+    uint4 xv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xv[v] = ld16(p + v * 8);
+    float bias = 0.0f;
+    uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 q = pair_permute(xv[v]);
+      bias = dot2_bf16(kBiasPair, q.x, bias);
+      bias = dot2_bf16(kBiasPair, q.y, bias);
+      bias = dot2_bf16(kBiasPair, q.z, bias);
+      bias = dot2_bf16(kBiasPair, q.w, bias);
+      dst[v] = q;
+    }
+    bsum[m * C + c] = bias;
+  }
+}
+
+// Per-row result callback: receives the lane-group totals (valid in lane
+// lk == 0) of both rows for grouped row p.
+struct GemvStore {
+  void* out;
+  int N;
+  template <int KIND>
+  __device__ __forceinline__ void put(size_t p, int u, float acc0, float acc1) const {
+    if (KIND == 0) {
+      static_cast<uint16_t*>(out)[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0, acc1));
+    } else {
+      *reinterpret_cast<float2*>(static_cast<float*>(out) + p * N + 2 * u) =
+          make_float2(acc0, acc1);
+    }
+  }
+};
+
+// One block's GEMV work for expert e, output tile `tile`.
+//   A:    KIND 0: x [T][K] (all T rows are staged, x_staged tells whether the
+//         caller already did it); KIND 1: h [R][K] (rows p0.. are staged here).
+//   offs: expert offsets (global or LDS); sorted: grouped slot -> flat slot.
+// Returns M (rows of the expert) so callers can run epilogues.
+template <int KIND, int LK, int NB, bool PIPE>
+__device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
+                                           const uint8_t* __restrict__ W,
+                                           const uint16_t* __restrict__ S, int e, int tile,
+                                           int p0, int M, const int* sorted, int K, int N,
+                                           int topk, int T, bool x_staged, uint32_t* xs,
+                                           float* bsum, int* tok, const GemvStore& st) {
+  constexpr int MAXM = kGemvMaxM;
+  constexpr int G = GemvGeom<KIND, LK>::G;
+  constexpr int UB = GemvGeom<KIND, LK>::UB;
+  const int C = K / 32;     // 16-byte code chunks per row
+  const int nch = C / LK;   // chunks per lane (uniform)
+  const int units = N / 2;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int g = lane / LK, lk = lane % LK;
@@ -114,38 +157,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
     }
   };
   load_batch(0, qa0, qa1, sa);
+  if (KIND == 0 && !x_staged) gemv_stage(A, T, K, xs, bsum);
 
-  const int p0 = offsets[e];
-  const int M = offsets[e + 1] - p0;
-
-  // stage activation rows: 32 values per (row, chunk), pair-permuted, plus the
-  // chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the main loop
-  // (so all-8 codes cancel to an exact zero)
-  auto stage = [&](int nrows, int m0) {
-    for (int i = tid; i < nrows * C; i += kThreads) {
-      const int m = i / C, c = i - m * C;
-      const uint16_t* src = (KIND == 0) ? A + static_cast<size_t>(m) * K + c * 32
-                                        : A + static_cast<size_t>(p0 + m0 + m) * K + c * 32;
-      uint4 xv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xv[v] = ld16(src + v * 8);
-      float bias = 0.0f;
-      uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 p = pair_permute(xv[v]);
-        bias = dot2_bf16(kBiasPair, p.x, bias);
-        bias = dot2_bf16(kBiasPair, p.y, bias);
-        bias = dot2_bf16(kBiasPair, p.z, bias);
-        bias = dot2_bf16(kBiasPair, p.w, bias);
-        dst[v] = p;
-      }
-      bsum[m * C + c] = bias;
-    }
-  };
-  if (KIND == 0) stage(T, 0);
-
-  // one 16-byte chunk (32 codes) of both rows against one staged activation row
+  // one 16-byte chunk (32 codes) of both rows against one staged row
   auto dot_chunk = [&](const uint4& q0, const uint4& q1, int xr, int c, float& d0, float& d1) {
     const uint4* xp = reinterpret_cast<const uint4*>(xs + xr * (K / 2) + c * 16);
 #pragma unroll
@@ -174,24 +188,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
       acc0 += wave_shfl_xor(acc0, sh);
       acc1 += wave_shfl_xor(acc1, sh);
     }
-    if (lk == 0 && valid) {
-      const size_t p = static_cast<size_t>(p0 + m);
-      if (KIND == 0) {
-        static_cast<uint16_t*>(out)[p * (N / 2) + u] = f32_to_bf16(silu_mul(acc0, acc1));
-      } else {
-        *reinterpret_cast<float2*>(static_cast<float*>(out) + p * N + 2 * u) =
-            make_float2(acc0, acc1);
-      }
-    }
+    if (lk == 0 && valid) st.put<KIND>(static_cast<size_t>(p0 + m), u, acc0, acc1);
   };
 
   // rows are taken in chunks of MAXM (normally one chunk: M <= T <= 4)
   for (int m0 = 0; m0 < M; m0 += MAXM) {
     const int Mc = min(MAXM, M - m0);
     if (KIND == 0) {
-      if (tid < Mc) tok[tid] = sorted_slot[p0 + m0 + tid] / topk;
+      if (tid < Mc) tok[tid] = sorted[p0 + m0 + tid] / topk;
     } else {
-      stage(Mc, m0);
+      gemv_stage(A + static_cast<size_t>(p0 + m0) * K, Mc, K, xs, bsum);
     }
     __syncthreads();
     if (!PIPE) {
@@ -255,17 +261,291 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
   }
 }
 
+// Dynamic LDS of a GEMV block: staged rows (pair-permuted) + bias sums.
+inline size_t gemv_lds_bytes(int rows, int K) {
+  return static_cast<size_t>(rows) * (K / 2) * 4 + static_cast<size_t>(rows) * (K / 32) * 4;
+}
+
+// Stand-alone grouped GEMV (moe_grouped_w4a16_ffn at small T): the expert of
+// block slot a comes from the permutation's active list.
+template <int KIND, int LK, int NB, bool PIPE>
+__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
+    const uint16_t* __restrict__ S, const int* __restrict__ offsets,
+    const int* __restrict__ sorted_slot, const int* __restrict__ active,
+    const int* __restrict__ n_active, void* __restrict__ out, int K, int N, int topk,
+    int tiles, int T) {
+  const int a = blockIdx.x / tiles;
+  const int tile = blockIdx.x - a * tiles;
+  const int na = *n_active;
+  const int e = active[a];  // in bounds: the grid has min(E, R) slots
+  if (a >= na) return;      // uniform per block, before any barrier
+  extern __shared__ uint32_t lds[];
+  const int rows_staged = (KIND == 0) ? T : kGemvMaxM;
+  uint32_t* xs = lds;
+  float* bsum = reinterpret_cast<float*>(lds + rows_staged * (K / 2));
+  __shared__ int tok[kGemvMaxM];
+  const int p0 = offsets[e];
+  const int M = offsets[e + 1] - p0;
+  gemv_block<KIND, LK, NB, PIPE>(A, W, S, e, tile, p0, M, sorted_slot, K, N, topk, T, false, xs,
+                                 bsum, tok, GemvStore{out, N});
+}
+
+// ----------------------------------------------------- fused decode layer ----
+// Whole layer for T <= 4 in two kernels (moe_layer_w4a16 at small T).
+//
+// decode_gateup_kernel: every block routes all T tokens itself (one wave per
+// token, the routing of moe_route_topk) and builds the permutation in LDS
+// (the stable counting sort of moe_permute), then runs its gate/up GEMV tile.
+// Block 0 writes the routing outputs and a compact per-expert record
+// {e, p0, M} for the second kernel.
+//
+// decode_down_kernel: a block owns a tile of NR output rows of H for every
+// active expert. Its lane groups walk the (expert, row pair) work items of the
+// tile with the next item's codes in flight, read the expert's h rows from
+// LDS (all R = T*k grouped rows are staged once) and keep every result in
+// LDS, so the block ends holding all k expert outputs of every token for its
+// rows: the combine out[t] = sum_j w[t,j] y[t,j] is then taken in increasing
+// j inside the block, in the order moe_combine uses. No counters, fences or
+// atomics cross blocks.
+constexpr int kDecodeMaxT = 4;
+constexpr int kDecodeMaxR = kDecodeMaxT * 32;
+constexpr int kDecodeBlocks = 256;   // target blocks of the down kernel
+
+template <int LK, int NB, bool PIPE, int S>
+__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
+    int k, int tiles, int* __restrict__ ids_out, float* __restrict__ w_out,
+    int* __restrict__ offsets_out, int* __restrict__ sorted_out, int* __restrict__ pos_out,
+    int* __restrict__ active_out, int* __restrict__ n_active_out, uint16_t* __restrict__ h,
+    int* __restrict__ rec) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* xs = lds;                                            // [T][H/2]
+  float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][H/32]
+  int* s_off = reinterpret_cast<int*>(bsum + T * (H / 32));      // [E + 1]: counts, then offsets
+  __shared__ int s_ids[kDecodeMaxR];
+  __shared__ float s_w[kDecodeMaxR];
+  __shared__ int s_sorted[kDecodeMaxR];
+  __shared__ int s_pos[kDecodeMaxR];
+  __shared__ int s_act[kDecodeMaxR];
+  __shared__ int s_tot[4];
+  __shared__ int tok[kGemvMaxM];
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int R = T * k;
+
+  // x rows do not depend on routing: stage them first
+  gemv_stage(x, T, H, xs, bsum);
+  for (int i = tid; i <= E; i += kThreads) s_off[i] = 0;
+  if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
+  __syncthreads();
+  if (tid < R) atomicAdd(&s_off[s_ids[tid]], 1);
+  __syncthreads();
+  // counts -> exclusive offsets and the active list (E <= 1024: 4 per thread)
+  const int ept = (E + kThreads - 1) / kThreads;
+  int c[4], sc = 0, sf = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * ept + i;
+    c[i] = (i < ept && e < E) ? s_off[e] : 0;
+    sc += c[i];
+    sf += c[i] > 0;
+  }
+  int tot_c, na;
+  int oc = block256_excl_scan(sc, s_tot, tot_c);
+  int of = block256_excl_scan(sf, s_tot, na);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * ept + i;
+    if (i < ept && e < E) {
+      s_off[e] = oc;
+      if (c[i]) s_act[of] = e;
+    }
+    oc += c[i];
+    of += c[i] > 0;
+  }
+  if (tid == 0) s_off[E] = R;
+  __syncthreads();
+  // stable position of slot f: its expert's offset + earlier slots of that expert
+  if (tid < R) {
+    const int id = s_ids[tid];
+    int before = 0;
+    for (int f = 0; f < tid; ++f) before += (s_ids[f] == id);
+    const int p = s_off[id] + before;
+    s_sorted[p] = tid;
+    s_pos[tid] = p;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < R; i += kThreads) {
+      ids_out[i] = s_ids[i];
+      w_out[i] = s_w[i];
+      sorted_out[i] = s_sorted[i];
+      pos_out[i] = s_pos[i];
+    }
+    for (int i = tid; i <= E; i += kThreads) offsets_out[i] = s_off[i];
+    for (int i = tid; i < na; i += kThreads) {
+      const int e = s_act[i];
+      active_out[i] = e;
+      rec[1 + 3 * i] = e;
+      rec[2 + 3 * i] = s_off[e];
+      rec[3 + 3 * i] = s_off[e + 1] - s_off[e];
+    }
+    if (tid == 0) {
+      *n_active_out = na;
+      rec[0] = na;
+    }
+  }
+  const int a = blockIdx.x / tiles;
+  if (a >= na) return;  // uniform per block
+  const int tile = blockIdx.x - a * tiles;
+  const int e = s_act[a];
+  const int p0 = s_off[e];
+  const int M = s_off[e + 1] - p0;
+  gemv_block<0, LK, NB, PIPE>(x, w13, s13, e, tile, p0, M, s_sorted, H, 2 * I, k, T, true, xs,
+                              bsum, tok, GemvStore{h, 2 * I});
+}
+
+// NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
+// separate calls).
+template <int LK, int NB>
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
+    const uint16_t* __restrict__ s2, int T, int H, int I, int k, int upb,
+    const int* __restrict__ rec, const int* __restrict__ slot_pos,
+    const float* __restrict__ topk_w, float* __restrict__ y, float* __restrict__ out) {
+  constexpr int G = kWave / LK;       // lane groups per wave
+  constexpr int NG = 4 * G;           // lane groups per block
+  extern __shared__ uint32_t lds[];
+  const int R = T * k;
+  const int C = I / 32;
+  const int nr = 2 * upb;                                        // rows of H in this tile
+  uint32_t* xs = lds;                                            // [R][I/2]
+  float* bsum = reinterpret_cast<float*>(lds + R * (I / 2));     // [R][C]
+  float* ybuf = bsum + R * C;                                    // [R][nr]
+  __shared__ int s_e[kDecodeMaxR], s_p0[kDecodeMaxR], s_m[kDecodeMaxR];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  const int lg = wv * G + lane / LK, lk = lane % LK;
+  const int u0 = blockIdx.x * upb;                 // first unit (row pair) of the tile
+  const int units = H / 2;
+
+  const int na = rec[0];
+  for (int i = tid; i < na; i += kThreads) {
+    s_e[i] = rec[1 + 3 * i];
+    s_p0[i] = rec[2 + 3 * i];
+    s_m[i] = rec[3 + 3 * i];
+  }
+  gemv_stage(h, R, I, xs, bsum);
+  __syncthreads();
+
+  // work item q = (active expert a, unit uu of the tile)
+  const int nitems = na * upb;
+  const size_t rowb = static_cast<size_t>(I / 2), srow = static_cast<size_t>(I / kGroup);
+  auto item_rows = [&](int q, int& e, int& u) {
+    const int a = q / upb;
+    const int uu = q - a * upb;
+    e = s_e[a];
+    u = min(u0 + uu, units - 1);
+  };
+  uint4 qa0[NB], qa1[NB], qb0[NB], qb1[NB];
+  uint32_t sa[NB], sb[NB];
+  auto load_item = [&](int q, uint4 (&q0)[NB], uint4 (&q1)[NB], uint32_t (&sc)[NB]) {
+    int e, u;
+    item_rows(min(q, nitems - 1), e, u);
+    const uint8_t* W0 = w2 + (static_cast<size_t>(e) * H + 2 * u) * rowb + lk * 16;
+    const uint16_t* S0 = s2 + (static_cast<size_t>(e) * H + 2 * u) * srow;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      q0[b] = ld16(W0 + b * LK * 16);
+      q1[b] = ld16(W0 + rowb + b * LK * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = lk + b * LK;
+      sc[b] = static_cast<uint32_t>(S0[c >> 2]) | (static_cast<uint32_t>(S0[srow + (c >> 2)]) << 16);
+    }
+  };
+  auto run_item = [&](int q, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
+                      const uint32_t (&sc)[NB]) {
+    const int a = q / upb;
+    const int uu = q - a * upb;
+    const int p0 = s_p0[a], M = s_m[a];
+    const bool valid = u0 + uu < units;
+    for (int m = 0; m < M; ++m) {
+      const int xr = p0 + m;
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = lk + b * LK;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + xr * (I / 2) + c * 16);
+        float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 xv = xp[v];
+          uint32_t c0 = (&q0[b].x)[v], c1 = (&q1[b].x)[v];
+          asm volatile("" : "+v"(c0), "+v"(c1));
+          uint32_t a0, a1, a2, a3;
+          nibble_pairs(c0, a0, a1, a2, a3);
+          d0 = dot2_bf16(a0, xv.x, d0);
+          d0 = dot2_bf16(a1, xv.y, d0);
+          d0 = dot2_bf16(a2, xv.z, d0);
+          d0 = dot2_bf16(a3, xv.w, d0);
+          nibble_pairs(c1, a0, a1, a2, a3);
+          d1 = dot2_bf16(a0, xv.x, d1);
+          d1 = dot2_bf16(a1, xv.y, d1);
+          d1 = dot2_bf16(a2, xv.z, d1);
+          d1 = dot2_bf16(a3, xv.w, d1);
+        }
+        const float cs = bsum[xr * C + c];
+        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu)) * (d0 - cs);
+        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16)) * (d1 - cs);
+      }
+#pragma unroll
+      for (int sh = LK / 2; sh >= 1; sh >>= 1) {
+        acc0 += wave_shfl_xor(acc0, sh);
+        acc1 += wave_shfl_xor(acc1, sh);
+      }
+      if (lk == 0 && valid) {
+        ybuf[xr * nr + 2 * uu] = acc0;
+        ybuf[xr * nr + 2 * uu + 1] = acc1;
+        *reinterpret_cast<float2*>(y + static_cast<size_t>(xr) * H + 2 * (u0 + uu)) =
+            make_float2(acc0, acc1);
+      }
+    }
+  };
+  // items lg, lg + NG, ...: two register sets alternate so the next item's
+  // codes stream while the current one is computed
+  if (lg < nitems) load_item(lg, qa0, qa1, sa);
+  for (int q = lg; q < nitems; q += 2 * NG) {
+    if (q + NG < nitems) load_item(q + NG, qb0, qb1, sb);
+    run_item(q, qa0, qa1, sa);
+    if (q + 2 * NG < nitems) load_item(q + 2 * NG, qa0, qa1, sa);
+    if (q + NG < nitems) run_item(q + NG, qb0, qb1, sb);
+  }
+  __syncthreads();
+  // combine for this tile's rows, in increasing j
+  for (int idx = tid; idx < T * nr; idx += kThreads) {
+    const int t = idx / nr, r = idx - t * nr;
+    const int n = 2 * u0 + r;
+    if (n >= H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float wj = topk_w[t * k + j];
+      acc += wj * ybuf[slot_pos[t * k + j] * nr + r];
+    }
+    out[static_cast<size_t>(t) * H + n] = acc;
+  }
+}
+
 template <int KIND, int LK, int NB, bool PIPE>
 hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                          const int* offsets, const int* sorted_slot, const int* active,
                          const int* n_active, void* out, int K, int N, int topk,
                          int max_active, int T, hipStream_t s) {
-  constexpr int UB = (kThreads / kWave) * (kWave / LK);
+  constexpr int UB = GemvGeom<KIND, LK>::UB;
   const int units = N / 2;
   const int tiles = (units + UB - 1) / UB;
-  const int rows_staged = (KIND == 0) ? T : kGemvMaxM;
-  const size_t lds = static_cast<size_t>(rows_staged) * (K / 2) * 4 +
-                     static_cast<size_t>(rows_staged) * (K / 32) * 4;
+  const size_t lds = gemv_lds_bytes((KIND == 0) ? T : kGemvMaxM, K);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&w4a16_gemv_kernel<KIND, LK, NB, PIPE>),
@@ -278,40 +558,107 @@ hipError_t launch_gemv_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
   return hipGetLastError();
 }
 
-template <int KIND, int LK>
-hipError_t launch_gemv_lk(const uint16_t* A, const uint8_t* W, const uint16_t* S,
-                          const int* offsets, const int* sorted_slot, const int* active,
-                          const int* n_active, void* out, int K, int N, int topk,
-                          int max_active, int T, hipStream_t s) {
-  const int nch = K / 32 / LK;
-#define MOE_GEMV_CASE(NB_, PIPE_)                                                              \
-  return launch_gemv_t<KIND, LK, NB_, PIPE_>(A, W, S, offsets, sorted_slot, active, n_active, \
-                                             out, K, N, topk, max_active, T, s)
-  switch (nch) {
-    case 1: MOE_GEMV_CASE(1, false);
-    case 2: MOE_GEMV_CASE(2, false);
-    case 3: MOE_GEMV_CASE(3, false);
-    case 4: MOE_GEMV_CASE(4, false);
-    default: MOE_GEMV_CASE(4, true);
+// Pick the lane split LK (largest of 16/8/4 dividing the chunk count) and the
+// batch shape, then call F<LK, NB, PIPE>::run(args...).
+template <template <int, int, bool> class F, typename... Args>
+hipError_t gemv_dispatch(int K, Args... args) {
+  const int C = K / 32;
+  const int LK = (C % 16 == 0 && C >= 64) ? 16 : (C % 8 == 0 ? 8 : 4);
+  const int nch = C / LK;
+#define MOE_GEMV_NB(LK_)                                          \
+  switch (nch) {                                                  \
+    case 1: return F<LK_, 1, false>::run(args...);                \
+    case 2: return F<LK_, 2, false>::run(args...);                \
+    case 3: return F<LK_, 3, false>::run(args...);                \
+    case 4: return F<LK_, 4, false>::run(args...);                \
+    default: return F<LK_, 4, true>::run(args...);                \
   }
-#undef MOE_GEMV_CASE
+  if (LK == 16) { MOE_GEMV_NB(16) }
+  if (LK == 8) { MOE_GEMV_NB(8) }
+  MOE_GEMV_NB(4)
+#undef MOE_GEMV_NB
 }
+
+template <int KIND>
+struct GemvLaunch {
+  template <int LK, int NB, bool PIPE>
+  struct F {
+    template <typename... A>
+    static hipError_t run(A... a) { return launch_gemv_t<KIND, LK, NB, PIPE>(a...); }
+  };
+};
+template <int LK, int NB, bool PIPE>
+using GemvLaunch0 = typename GemvLaunch<0>::template F<LK, NB, PIPE>;
+template <int LK, int NB, bool PIPE>
+using GemvLaunch1 = typename GemvLaunch<1>::template F<LK, NB, PIPE>;
 
 template <int KIND>
 hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                        const int* offsets, const int* sorted_slot, const int* active,
                        const int* n_active, void* out, int K, int N, int topk,
                        int max_active, int T, hipStream_t s) {
-  const int C = K / 32;
-  if (C % 16 == 0 && C >= 64)
-    return launch_gemv_lk<KIND, 16>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
-                                    topk, max_active, T, s);
-  if (C % 8 == 0)
-    return launch_gemv_lk<KIND, 8>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
-                                   topk, max_active, T, s);
-  return launch_gemv_lk<KIND, 4>(A, W, S, offsets, sorted_slot, active, n_active, out, K, N,
-                                 topk, max_active, T, s);
+  if (KIND == 0)
+    return gemv_dispatch<GemvLaunch0>(K, A, W, S, offsets, sorted_slot, active, n_active, out, K,
+                                      N, topk, max_active, T, s);
+  return gemv_dispatch<GemvLaunch1>(K, A, W, S, offsets, sorted_slot, active, n_active, out, K,
+                                    N, topk, max_active, T, s);
 }
+
+template <int LK, int NB, bool PIPE>
+struct DecodeGateupLaunch {
+  static hipError_t run(const float* logits, const uint16_t* x, const uint8_t* w13,
+                        const uint16_t* s13, int T, int H, int I, int E, int k, int* ids, float* w,
+                        int* offsets, int* sorted_slot, int* slot_pos, int* active, int* n_active,
+                        uint16_t* h, int* rec, int max_active, hipStream_t s) {
+    constexpr int UB = GemvGeom<0, LK>::UB;
+    const int tiles = (I + UB - 1) / UB;
+    const size_t lds = gemv_lds_bytes(T, H) + static_cast<size_t>(E + 1) * 4;
+    auto go = [&](auto kern) -> hipError_t {
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3(max_active * tiles), dim3(kThreads), lds, s, logits, x, w13,
+                         s13, T, H, I, E, k, tiles, ids, w, offsets, sorted_slot, slot_pos,
+                         active, n_active, h, rec);
+      return hipGetLastError();
+    };
+    if (E <= 256) return go(&decode_gateup_kernel<LK, NB, PIPE, 4>);
+    return go(&decode_gateup_kernel<LK, NB, PIPE, 16>);
+  }
+};
+
+// Down tile size: enough units per block for about kDecodeBlocks blocks.
+inline int decode_down_upb(int H) { return (H / 2 + kDecodeBlocks - 1) / kDecodeBlocks; }
+
+inline size_t decode_down_lds(int T, int H, int I, int k) {
+  const int R = T * k;
+  return gemv_lds_bytes(R, I) + static_cast<size_t>(R) * 2 * decode_down_upb(H) * 4;
+}
+
+template <int LK, int NB, bool PIPE>
+struct DecodeDownLaunch {
+  static hipError_t run(const uint16_t* h, const uint8_t* w2, const uint16_t* s2, int T, int H,
+                        int I, int k, const int* rec, const int* slot_pos, const float* w,
+                        float* y, float* out, hipStream_t s) {
+    if (PIPE) return hipErrorInvalidValue;  // excluded by the host dispatch rule
+    const int upb = decode_down_upb(H);
+    const int blocks = (H / 2 + upb - 1) / upb;
+    const size_t lds = decode_down_lds(T, H, I, k);
+    auto kern = &decode_down_kernel<LK, (NB < 1 ? 1 : NB)>;
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, k, upb, rec,
+                       slot_pos, w, y, out);
+    return hipGetLastError();
+  }
+};
 
 // ---------------------------------------------------------------- MFMA ----
 constexpr int kALd = kGroup + 8;  // LDS row stride of the activation tile (bf16)
@@ -557,6 +904,69 @@ hipError_t launch_w4a16_ffn(int T, int H, int I, int E, int k, const uint16_t* x
   err = launch_mfma_t<0, 2>(x, w13, s13, offsets, sorted_slot, h, H, 2 * I, E, k, T, s);
   if (err != hipSuccess) return err;
   return launch_mfma_t<1, 2>(h, w2, s2, offsets, sorted_slot, y, I, H, E, k, T, s);
+}
+
+// ------------------------------------------------------------ whole layer ----
+namespace {
+struct LayerWs {
+  uint16_t* h;
+  int* rec;
+  void* perm;
+};
+LayerWs layer_carve(void* ws, int T, int I, int E, int k) {
+  const size_t R = static_cast<size_t>(T) * k;
+  const size_t act = R < static_cast<size_t>(E) ? R : static_cast<size_t>(E);
+  char* p = static_cast<char*>(ws);
+  LayerWs w;
+  w.h = reinterpret_cast<uint16_t*>(p);
+  p += align_up(R * I * sizeof(uint16_t), 256);
+  w.rec = reinterpret_cast<int*>(p);
+  p += align_up((1 + 3 * act) * sizeof(int), 256);
+  w.perm = p;
+  return w;
+}
+// The two-kernel decode layer: T <= 4, the down kernel's codes fit one
+// register batch (I / 32 / LK <= 4) and its staged h rows fit LDS.
+bool layer_fused(int T, int H, int I, int k) {
+  if (T > kDecodeMaxT || T * k > kDecodeMaxR) return false;
+  const int C = I / 32;
+  const int LK = (C % 16 == 0 && C >= 64) ? 16 : (C % 8 == 0 ? 8 : 4);
+  if (C / LK > 4) return false;
+  return decode_down_lds(T, H, I, k) <= 150 * 1024;
+}
+}  // namespace
+
+size_t w4a16_layer_workspace_bytes(int T, int, int I, int E, int k) {
+  const size_t R = static_cast<size_t>(T) * k;
+  const size_t act = R < static_cast<size_t>(E) ? R : static_cast<size_t>(E);
+  return align_up(R * I * sizeof(uint16_t), 256) + align_up((1 + 3 * act) * sizeof(int), 256) +
+         align_up(permute_workspace_bytes(T, E, k), 256);
+}
+
+hipError_t launch_w4a16_layer(int T, int H, int I, int E, int k, const float* logits,
+                              const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                              const uint8_t* w2, const uint16_t* s2, int* ids, float* w,
+                              int* offsets, int* sorted_slot, int* slot_pos, int* active,
+                              int* n_active, float* y, float* out, void* ws, hipStream_t s) {
+  const LayerWs lw = layer_carve(ws, T, I, E, k);
+  if (T > 0 && layer_fused(T, H, I, k)) {
+    const int R = T * k;
+    const int max_active = R < E ? R : E;
+    hipError_t err = gemv_dispatch<DecodeGateupLaunch>(
+        H, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets, sorted_slot, slot_pos, active,
+        n_active, lw.h, lw.rec, max_active, s);
+    if (err != hipSuccess) return err;
+    return gemv_dispatch<DecodeDownLaunch>(I, lw.h, w2, s2, T, H, I, k, lw.rec, slot_pos, w, y,
+                                           out, s);
+  }
+  hipError_t err = launch_route_topk(logits, T, E, k, ids, w, s);
+  if (err != hipSuccess) return err;
+  err = launch_permute(ids, T, E, k, offsets, sorted_slot, slot_pos, active, n_active, lw.perm, s);
+  if (err != hipSuccess) return err;
+  err = launch_w4a16_ffn(T, H, I, E, k, x, w13, s13, w2, s2, offsets, sorted_slot, active,
+                         n_active, y, lw.h, s);
+  if (err != hipSuccess) return err;
+  return launch_combine(y, slot_pos, w, T, H, k, out, s);
 }
 
 }  // namespace moe

@@ -32,7 +32,7 @@ def header_functions():
 @needs_lib
 def test_exports_match_header():
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(LIB, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -157,3 +157,26 @@ def test_binding_raises_moe_error():
     assert ei.value.status == 2
     with pytest.raises(ValueError):          # buffer smaller than the call needs
         _lib.route_topk(t, 2, torch.empty(7), out, stream=0)
+
+
+@needs_lib
+def test_layer_w4a16_validation():
+    f = LIB.moe_layer_w4a16
+    s = _shape()
+    need = _lib.layer_w4a16_workspace(4, 256, 128, 8, 2)
+    assert need > 0
+    ok = [A] * 15       # logits, x, w13, s13, w2, s2, ids, w, offsets, sorted, pos, active, n_active, y, out
+    assert f(ctypes.byref(_shape(H=200)), *ok, A, need, None) == 2
+    assert f(ctypes.byref(s), *ok, A, need - 1, None) == 4
+    bad = list(ok)
+    bad[0] = MIS
+    assert f(ctypes.byref(s), *bad, A, need, None) == 3
+    bad[0] = None
+    assert f(ctypes.byref(s), *bad, A, need, None) == 1
+    if _no_gpu():
+        assert f(ctypes.byref(s), *ok, A, need, None) == 6
+    # the Python wrapper marshals the same 20 arguments
+    import torch
+    dummy = torch.empty(64, dtype=torch.uint8)
+    with pytest.raises(_lib.MoeError):
+        _lib.layer_w4a16((4, 200, 128, 8, 2), *([dummy] * 15), dummy, stream=0)

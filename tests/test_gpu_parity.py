@@ -292,3 +292,90 @@ def test_empty_batch_all_entry_points():
         moe.moe_forward(b, x, L, (dummy, dummy, dummy, dummy))
         torch.cuda.synchronize()
         assert np.all(to_np(b.offsets) == 0) and int(to_np(b.n_active)[0]) == 0
+
+
+# ------------------------------------------------------------ whole layer --
+def _layer_entry(wl, x, L, weights):
+    import quantized_moe_expert_top_amd as moe
+    b = moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, "w4a16")
+    moe.moe_layer(b, to_dev(x), to_dev(L), weights)
+    torch.cuda.synchronize()
+    R = wl.T * wl.k
+    n = int(to_np(b.n_active)[0])
+    return {"ids": to_np(b.ids), "w": to_np(b.w), "expert_offsets": to_np(b.offsets),
+            "sorted_slot": to_np(b.sorted_slot)[:R], "slot_pos": to_np(b.slot_pos)[:R],
+            "n_active": n, "active": to_np(b.active)[:n],
+            "y": to_np(b.y)[:R].astype(np.float64), "out": to_np(b.out).astype(np.float64),
+            "y_bits": to_np(b.y)[:R].copy(), "out_bits": to_np(b.out).view(np.uint32).copy()}
+
+
+LAYER_CASES = [
+    # name, wid, T, H, I, E, k
+    ("layer_t1", 301, 1, 256, 128, 8, 2),
+    ("layer_t3_ragged", 302, 3, 384, 384, 16, 4),
+    ("layer_t4_k32", 303, 4, 256, 256, 64, 32),     # R = 128: the largest fused batch
+    ("layer_t4_e1024", 304, 4, 512, 256, 1024, 8),
+    ("layer_t9_unfused", 305, 9, 256, 128, 8, 2),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_entry_matches_oracle_and_calls(case):
+    name, wid, T, H, I, E, k = case
+    wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
+    x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+    ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, 0))
+    wts = stage_weights(wl, 0)
+    _say("layer entry", name, (T, H, I, E, k))
+    got = _layer_entry(wl, x, L, wts)
+    check_routing_and_perm(got, ref)
+    assert_close(got["y"], ref["y"], "y")
+    assert_close(got["out"], ref["out"], "out")
+    calls = run_layer(wl, x, L, wts)
+    np.testing.assert_array_equal(got["y_bits"], calls["y_bits"])
+    np.testing.assert_array_equal(got["out_bits"], calls["out_bits"])
+
+
+@pytest.mark.parametrize("name,unit", [("decode_t2", 0), ("decode_t2", 17), ("decode_large", 5),
+                                       ("tiny", 0)])
+def test_layer_entry_workloads(name, unit):
+    wl = synth.workload(name)
+    x, L = synth.x_bf16(wl, unit), synth.router_logits(wl, unit)
+    ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, unit))
+    wts = stage_weights(wl, unit, ref["perm"]["active"])
+    _say("layer entry", name, unit)
+    got = _layer_entry(wl, x, L, wts)
+    check_routing_and_perm(got, ref)
+    assert_close(got["out"], ref["out"], "out")
+    again = _layer_entry(wl, x, L, wts)
+    np.testing.assert_array_equal(got["out_bits"], again["out_bits"])
+
+
+def test_layer_entry_in_graph_replays():
+    """The fused decode layer captured in a HIP graph: every replay matches the
+    eager result (the combine counters are cleared inside the layer each time)."""
+    import quantized_moe_expert_top_amd as moe
+    wl = synth.workload("decode_t2")
+    units = [0, 1, 2]
+    bufs, ins = [], []
+    for u in units:
+        x, L = synth.x_bf16(wl, u), synth.router_logits(wl, u)
+        ins.append((to_dev(x), to_dev(L), stage_weights(wl, u)))
+        bufs.append(moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, "w4a16"))
+    eager = []
+    for b, (x, L, w) in zip(bufs, ins):
+        moe.moe_layer(b, x, L, w)
+    torch.cuda.synchronize()
+    eager = [to_np(b.out).view(np.uint32).copy() for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b, (x, L, w) in zip(bufs, ins):
+            moe.moe_layer(b, x, L, w)
+    for rep in range(3):
+        for b in bufs:
+            b.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(bufs):
+            np.testing.assert_array_equal(to_np(b.out).view(np.uint32), eager[i])
