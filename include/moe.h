@@ -36,7 +36,8 @@
  *   - Calls on distinct streams with distinct workspaces may run concurrently.
  *   - Numerics are deterministic: integer atomics only (counts, maxima), no
  *     float atomics; two runs on the same inputs give identical bits.
- *   - T = 0 is a valid empty batch. T*k*H must stay below 2^31.
+ *   - T = 0 is a valid empty batch. T*k*max(H, I) and 2*H*I must stay below
+ *     2^31 (32-bit element offsets).
  *   - Out-of-range expert ids or non-finite logits are outside the contract.
  */
 #ifndef MOE_H

@@ -72,9 +72,13 @@ int check_shape(const moe_shape* s, int hmod, int imod) {
   if (st) return st;
   if (s->H < hmod || s->H % hmod) return fail(MOE_ESHAPE, "H = %d must be a positive multiple of %d", s->H, hmod);
   if (s->I < imod || s->I % imod) return fail(MOE_ESHAPE, "I = %d must be a positive multiple of %d", s->I, imod);
-  if (static_cast<long long>(s->T) * s->k * s->H >= (1LL << 31))
-    return fail(MOE_ESHAPE, "T*k*H = %lld too large for int32 row indexing",
-                static_cast<long long>(s->T) * s->k * s->H);
+  const long long hi = s->H > s->I ? s->H : s->I;
+  if (static_cast<long long>(s->T) * s->k * hi >= (1LL << 31))
+    return fail(MOE_ESHAPE, "T*k*max(H, I) = %lld too large for 32-bit offsets",
+                static_cast<long long>(s->T) * s->k * hi);
+  if (2LL * s->H * s->I >= (1LL << 31))
+    return fail(MOE_ESHAPE, "2*H*I = %lld too large for 32-bit offsets into one expert",
+                2LL * s->H * s->I);
   return MOE_OK;
 }
 

@@ -64,8 +64,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// silu(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal
+// (about 1 ulp each). g -> -inf gives e^-g = inf and a zero reciprocal.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 template <typename T>
@@ -158,6 +161,14 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     w[lane] = z / sum;
   }
 }
+
+// Raw buffer resource over [base, base + bytes) for buffer loads (untyped,
+// 32-bit data format, no swizzle); loads at offsets past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 16-byte global load (global_load_dwordx4).
 __device__ __forceinline__ uint4 ld16(const void* p) {

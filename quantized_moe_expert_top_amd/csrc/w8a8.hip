@@ -4,12 +4,12 @@
 // a prompt run as grouped int8 tensor-core GEMMs. Here:
 //   1. act_quant: per token row, s = absmax/127 (IEEE float32 division), codes
 //      rint(x/s) clamped to [-127, 127] (round half to even).
-//   2. gate/up: v_mfma_i32_32x32x32_i8 over (expert, 128-row, 64-column) tiles;
+//   2. gate/up: v_mfma_i32_32x32x32_i8 over (expert, 128-row, 128-column) tiles;
 //      the epilogue dequantizes (acc * xs[t] * s13[e,n]) and applies SwiGLU in
 //      float32, writing h (float32) in grouped order.
 //   3. h_quant: the same per-row rule on h (one row per routed slot). h stays
 //      float32 until here so the code decisions match a float32 reference.
-//   4. down: int8 MFMA over (expert, 128-row, 128-column) tiles; y = acc *
+//   4. down: int8 MFMA over (expert, 128-row, 256-column) tiles; y = acc *
 //      hs[p] * s2[e,n], stored float32.
 // The int32 accumulators are exact, so they are reproducible bit for bit.
 #include "common.h"
@@ -22,7 +22,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBM = 128;        // rows per tile
 constexpr int kBK = 64;         // K per pipeline step (two MFMA k-steps of 32)
-constexpr int kLd = kBK + 16;   // LDS row stride in bytes (bank spread)
 
 // --------------------------------------------------------- quantization ----
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
@@ -108,24 +107,42 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------- int8 GEMM ----
-// KIND 0: gate/up. Tile = 128 rows x 64 h-columns; wave (wm, wn) owns rows
-//         [64wm, +64) and h-columns [32wn, +32): B subtile 0 = gate rows,
-//         subtile 1 = the matching up rows. Out: h float32 [R, I].
-// KIND 1: down. Tile = 128 rows x 128 W2 rows; wave (wm, wn) owns rows
-//         [64wm, +64) and W2 rows [64wn, +64) as two subtiles. Out: y float32.
-// LDS holds the A tile (128 x 64 int8) and the B tile (128 W rows x 64 int8)
-// per pipeline step, double-buffered. Operand k order inside one MFMA step:
-// lane half hf = lane/32 takes k = 32*ks + 16*hf + [0, 16).
+// KIND 0: gate/up. Tile = 128 rows x 128 h-columns: the B tile holds the 128
+//         gate rows and the 128 matching up rows (256 W13 rows). Wave (wm, wn)
+//         owns rows [64wm, +64) and h-columns [64wn, +64): subtiles 0,1 gate,
+//         2,3 the matching up rows. Out: h float32 [R, I].
+// KIND 1: down. Tile = 128 rows x 256 W2 rows; wave (wm, wn) owns rows
+//         [64wm, +64) and W2 rows [128wn, +128) as four subtiles. Out: y.
+// Pipeline: K advances in 64-byte stages; kW8Stages stages are in flight,
+// each moved HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging;
+// the buffer form, unlike the global one, leaves LDS reads countable in order,
+// so operand reads overlap the MFMAs). A wave
+// instruction fills 64 consecutive 16-byte LDS slots; slot s of a tile holds
+// row s/4, chunk (s%4) ^ ((row/4)%4), so each row's 64 bytes are still read as
+// one coalesced run while the MFMA operand reads (32 rows, one chunk each) hit
+// distinct LDS banks. Waits are explicit (vmcnt + barrier) so loads of later
+// stages stay in flight across the barrier.
+// MFMA operand k order inside one 32-k step: lane half hf = lane/32 takes
+// k = 32*ks + 16*hf + [0, 16).
+constexpr int kW8Stages = 3;
+constexpr int kW8BN = 256;                       // B rows per tile
+constexpr int kW8ASlots = kBM * 4;               // 16-byte slots per stage
+constexpr int kW8BSlots = kW8BN * 4;
+constexpr int kW8StageBytes = (kW8ASlots + kW8BSlots) * 16;
+
+__device__ __forceinline__ int swz(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+
 template <int KIND>
-__global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const int8_t* __restrict__ W, const float* __restrict__ w_scale,
-    const int* __restrict__ offsets, const int* __restrict__ sorted_slot, int K, int N, int E,
-    int topk, int NT, float* __restrict__ h_out, float* __restrict__ y_out,
+    const int* __restrict__ offsets, const int* __restrict__ sorted_slot, int a_rows, int K,
+    int N, int E, int topk, int NT, float* __restrict__ h_out, float* __restrict__ y_out,
     int32_t* __restrict__ dbg_acc) {
-  __shared__ __attribute__((aligned(16))) int8_t a_lds[2][kBM * kLd];
-  __shared__ __attribute__((aligned(16))) int8_t b_lds[2][kBM * kLd];
+  extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // kW8Stages * kW8StageBytes
   __shared__ int row_src[kBM];
+  __shared__ float row_scale[kBM];    // activation scale of each tile row
+  __shared__ float col_scale[kW8BN];  // weight scale of each B tile row
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[3];
 
@@ -137,93 +154,120 @@ __global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
   const int wm = wv >> 1, wn = wv & 1;
   const int I = N / 2;  // KIND 0 only
 
-  // source row of each A tile row (token for gate/up, grouped row for down)
-  if (tid < kBM) {
-    const int p = ti.p_begin + tid;
-    row_src[tid] = (p < ti.p_end) ? ((KIND == 0) ? sorted_slot[p] / topk : p) : -1;
-  }
-  // W row held at B tile row j (0..127)
+  // W row held at B tile row j (0..255)
   auto b_row = [&](int j) -> int {
     if (KIND == 0) {
-      const int half = j >> 6, c = ti.nt * 64 + (j & 63);
-      const int cc = c < I ? c : I - 1;
-      return half * I + cc;
-    } else {
-      const int r = ti.nt * 128 + j;
-      return r < N ? r : N - 1;
+      const int half = j >> 7, c = ti.nt * 128 + (j & 127);
+      return half * I + (c < I ? c : I - 1);
     }
+    const int r = ti.nt * kW8BN + j;
+    return r < N ? r : N - 1;
   };
+  // source row of each A tile row (token for gate/up, grouped row for down);
+  // rows past the expert's block read the tile's first row (results dropped).
+  // The scales the epilogue needs are staged here, off its critical path.
+  if (tid < kBM) {
+    const int p = ti.p_begin + tid;
+    const int pv = (p < ti.p_end) ? p : ti.p_begin;
+    const int src = (KIND == 0) ? sorted_slot[pv] / topk : pv;
+    row_src[tid] = src;
+    row_scale[tid] = a_scale[src];
+  }
+  col_scale[tid] = w_scale[static_cast<size_t>(ti.e) * N + b_row(tid)];
   __syncthreads();
 
-  // each thread moves 2 A chunks and 2 B chunks of 16 bytes per step
-  const int8_t* asrc[2];
-  const int8_t* bsrc[2];
-  int aoff[2];
+  // this thread's 2 A and 4 B slots per stage (slot = wave * 64 + lane + 256 * v),
+  // as byte offsets into buffer resources over A and this expert's W rows
+  const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(A, static_cast<uint32_t>(a_rows) * K);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      buffer_rsrc(W + static_cast<size_t>(ti.e) * N * K, static_cast<uint32_t>(N) * K);
+  uint32_t aoff[2], boff[4];
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
-    const int q = tid + kThreads * v;       // 0..511
-    const int r = q >> 2, ch = q & 3;       // row 0..127, 16-byte chunk 0..3
-    const int src = row_src[r];
-    asrc[v] = (src >= 0) ? A + static_cast<size_t>(src) * K + ch * 16 : nullptr;
-    bsrc[v] = W + (static_cast<size_t>(ti.e) * N + b_row(r)) * K + ch * 16;
-    aoff[v] = r * kLd + ch * 16;
+    const int s = tid + kThreads * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+    aoff[v] = static_cast<uint32_t>(row_src[row]) * K + c * 16;
   }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int s = tid + kThreads * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+    boff[v] = static_cast<uint32_t>(b_row(row)) * K + c * 16;
+  }
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto issue = [&](int st) {
+    uint8_t* base = w8_lds + (st % kW8Stages) * kW8StageBytes + wvu * kWave * 16;
+    const uint32_t k0 = static_cast<uint32_t>(st) * kBK;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_t*)(base + kThreads * v * 16), 16,
+                                               aoff[v] + k0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          b_rsrc, (lds_void_t*)(base + (kW8ASlots + kThreads * v) * 16), 16, boff[v] + k0, 0, 0, 0);
+  };
 
-  i32x16_t acc[2][2];
+  i32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  uint4 ar[2], br[2];
-  auto gload = [&](int step) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      ar[v] = asrc[v] ? ld16(asrc[v] + step * kBK) : make_uint4(0, 0, 0, 0);
-      br[v] = ld16(bsrc[v] + step * kBK);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      *reinterpret_cast<uint4*>(&a_lds[buf][aoff[v]]) = ar[v];
-      *reinterpret_cast<uint4*>(&b_lds[buf][aoff[v]]) = br[v];
-    }
-  };
-
   const int steps = K / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // land the epilogue's kernel arguments now: a scalar load still in flight
+  // inside the loop would turn every LDS wait there into a full drain
+  asm volatile("" ::"s"(h_out), "s"(y_out), "s"(dbg_acc));
+#pragma unroll
+  for (int st = 0; st < kW8Stages - 1; ++st)
+    if (st < steps) issue(st);
+
   for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < steps;
-    if (more) gload(st + 1);
+    // stage st is complete once at most the later in-flight stages remain
+    const int later = min(kW8Stages - 2, steps - 1 - st);
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (st + kW8Stages - 1 < steps) issue(st + kW8Stages - 1);
+    const uint8_t* base = w8_lds + (st % kW8Stages) * kW8StageBytes;
+    // all operand reads of the stage first: the second k-step's reads land
+    // while the first k-step's MFMAs run
+    i32x4_t aop[kBK / 32][2], bop[kBK / 32][4];
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      i32x4_t bop[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int brow = (KIND == 0) ? (j * 64 + wn * 32 + l32) : (wn * 64 + j * 32 + l32);
-        bop[j] = *reinterpret_cast<const i32x4_t*>(&b_lds[buf][brow * kLd + ks * 32 + hf * 16]);
-      }
+      const int c = 2 * ks + hf;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int arow = wm * 64 + i * 32 + l32;
-        const i32x4_t aop =
-            *reinterpret_cast<const i32x4_t*>(&a_lds[buf][arow * kLd + ks * 32 + hf * 16]);
+        aop[ks][i] = *reinterpret_cast<const i32x4_t*>(base + swz(arow, c) * 16);
+      }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const int brow = (KIND == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32)
+                                     : (wn * 128 + j * 32 + l32);
+        bop[ks][j] = *reinterpret_cast<const i32x4_t*>(base + (kW8ASlots + swz(brow, c)) * 16);
       }
     }
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[ks][i], bop[ks][j], acc[i][j], 0, 0, 0);
+    // keep that order through scheduling: 12 LDS reads, then 16 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   }
 
   // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4)
+  float cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int brow = (KIND == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32)
+                                 : (wn * 128 + j * 32 + l32);
+    cs[j] = col_scale[brow];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -231,28 +275,29 @@ __global__ __launch_bounds__(kThreads) void w8a8_mfma_kernel(
       const int m = wm * 64 + i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
       const int p = ti.p_begin + m;
       if (p >= ti.p_end) continue;
+      const float rs = row_scale[m];
       if (KIND == 0) {
-        const int n = ti.nt * 64 + wn * 32 + l32;
-        if (n >= I) continue;
-        const int ag = acc[i][0][r], au = acc[i][1][r];
-        if (dbg_acc) {
-          dbg_acc[static_cast<size_t>(p) * N + n] = ag;
-          dbg_acc[static_cast<size_t>(p) * N + I + n] = au;
-        }
-        const float xs = a_scale[row_src[m]];
-        const float g = static_cast<float>(ag) * xs * w_scale[static_cast<size_t>(ti.e) * N + n];
-        const float u = static_cast<float>(au) * xs * w_scale[static_cast<size_t>(ti.e) * N + I + n];
-        h_out[static_cast<size_t>(p) * I + n] = silu_mul(g, u);
-      } else {
-        const float hsv = a_scale[p];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = ti.nt * 128 + wn * 64 + j * 32 + l32;
+          if (n >= I) continue;
+          const int ag = acc[i][j][r], au = acc[i][j + 2][r];
+          if (dbg_acc) {
+            dbg_acc[static_cast<size_t>(p) * N + n] = ag;
+            dbg_acc[static_cast<size_t>(p) * N + I + n] = au;
+          }
+          const float g = static_cast<float>(ag) * rs * cs[j];
+          const float u = static_cast<float>(au) * rs * cs[j + 2];
+          h_out[static_cast<size_t>(p) * I + n] = silu_mul(g, u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = ti.nt * kW8BN + wn * 128 + j * 32 + l32;
           if (n >= N) continue;
           const int a = acc[i][j][r];
           if (dbg_acc) dbg_acc[static_cast<size_t>(p) * N + n] = a;
-          y_out[static_cast<size_t>(p) * N + n] =
-              static_cast<float>(a) * hsv * w_scale[static_cast<size_t>(ti.e) * N + n];
+          y_out[static_cast<size_t>(p) * N + n] = static_cast<float>(a) * rs * cs[j];
         }
       }
     }
@@ -264,14 +309,19 @@ hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t*
                             const float* w_scale, const int* offsets, const int* sorted_slot,
                             int K, int N, int E, int topk, int T, float* h_out, float* y_out,
                             int32_t* dbg_acc, hipStream_t s) {
-  const int NT = (KIND == 0) ? (N / 2 + 63) / 64 : (N + 127) / 128;
+  const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + kW8BN - 1) / kW8BN;
   const long long R = static_cast<long long>(T) * topk;
   const long long act = R < E ? R : E;
   const long long mt_up = (R + kBM - 1) / kBM + act;
   long long grid = (mt_up * NT + 7) / 8 * 8;
+  const size_t lds = static_cast<size_t>(kW8Stages) * kW8StageBytes;
+  const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&w8a8_mfma_kernel<KIND>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((w8a8_mfma_kernel<KIND>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     0, s, A, a_scale, W, w_scale, offsets, sorted_slot, K, N, E, topk, NT, h_out,
-                     y_out, dbg_acc);
+                     lds, s, A, a_scale, W, w_scale, offsets, sorted_slot,
+                     static_cast<int>(KIND == 0 ? T : R), K, N, E, topk, NT, h_out, y_out, dbg_acc);
   return hipGetLastError();
 }
 
