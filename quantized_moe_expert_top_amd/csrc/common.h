@@ -175,10 +175,11 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Block-wide exclusive scan of one int per thread for 256-thread blocks;
-// `wave_tot` is a 4-int LDS scratch. Contains two barriers: call it from all
-// threads of the block.
-__device__ __forceinline__ int block256_excl_scan(int v, int* wave_tot, int& total) {
+// Block-wide exclusive scan of one int per thread for NTHR-thread blocks;
+// `wave_tot` is an NTHR/64-int LDS scratch. Contains two barriers: call it
+// from all threads of the block.
+template <int NTHR>
+__device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -191,13 +192,16 @@ __device__ __forceinline__ int block256_excl_scan(int v, int* wave_tot, int& tot
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NTHR / kWave; ++i) {
     const int t = wave_tot[i];
     if (i < w) before += t;
     total += t;
   }
   __syncthreads();
   return before + incl - v;
+}
+__device__ __forceinline__ int block256_excl_scan(int v, int* wave_tot, int& total) {
+  return block_excl_scan<256>(v, wave_tot, total);
 }
 
 }  // namespace moe

@@ -58,10 +58,10 @@ constexpr int kGemvMaxT = 4;
 // PIPE: more than NB chunks per lane; two register batches alternate.
 constexpr int kGemvMaxM = 4;
 
-template <int KIND, int LK>
+template <int KIND, int LK, int NTHR = kThreads>
 struct GemvGeom {
-  static constexpr int G = kWave / LK;               // lane groups per wave
-  static constexpr int UB = (kThreads / kWave) * G;  // units per block
+  static constexpr int G = kWave / LK;            // lane groups per wave
+  static constexpr int UB = (NTHR / kWave) * G;   // units per block
 };
 
 // Stage activation rows into LDS: 32 values per (row, chunk), pair-permuted,
@@ -70,25 +70,36 @@ struct GemvGeom {
 // src + m * K.
 __device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int nrows, int K,
                                            uint32_t* xs, float* bsum) {
-  const int C = K / 32;
-  for (int i = threadIdx.x; i < nrows * C; i += kThreads) {
-    const int m = i / C, c = i - m * C;
-    const uint16_t* p = src + static_cast<size_t>(m) * K + c * 32;
-    uint4 xv[4];
+  const int C = K / 32, n = nrows * C, nt = blockDim.x;
+  // two (row, chunk) items per thread per pass, both loads issued before use
+  for (int i0 = threadIdx.x; i0 < n; i0 += 2 * nt) {
+    uint4 xv[2][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xv[v] = ld16(p + v * 8);
-    float bias = 0.0f;
-    uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+    for (int h = 0; h < 2; ++h) {
+      const int i = min(i0 + h * nt, n - 1);
+      const int m = i / C, c = i - m * C;
+      const uint16_t* p = src + static_cast<size_t>(m) * K + c * 32;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 q = pair_permute(xv[v]);
-      bias = dot2_bf16(kBiasPair, q.x, bias);
-      bias = dot2_bf16(kBiasPair, q.y, bias);
-      bias = dot2_bf16(kBiasPair, q.z, bias);
-      bias = dot2_bf16(kBiasPair, q.w, bias);
-      dst[v] = q;
+      for (int v = 0; v < 4; ++v) xv[h][v] = ld16(p + v * 8);
     }
-    bsum[m * C + c] = bias;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = i0 + h * nt;
+      if (i >= n) break;
+      const int m = i / C, c = i - m * C;
+      float bias = 0.0f;
+      uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 q = pair_permute(xv[h][v]);
+        bias = dot2_bf16(kBiasPair, q.x, bias);
+        bias = dot2_bf16(kBiasPair, q.y, bias);
+        bias = dot2_bf16(kBiasPair, q.z, bias);
+        bias = dot2_bf16(kBiasPair, q.w, bias);
+        dst[v] = q;
+      }
+      bsum[m * C + c] = bias;
+    }
   }
 }
 
@@ -111,9 +122,10 @@ struct GemvStore {
 // One block's GEMV work for expert e, output tile `tile`.
 //   A:    KIND 0: x [T][K] (all T rows are staged, x_staged tells whether the
 //         caller already did it); KIND 1: h [R][K] (rows p0.. are staged here).
-//   offs: expert offsets (global or LDS); sorted: grouped slot -> flat slot.
+//   sorted: flat slot of each of the expert's M rows (global or LDS); row m
+//   is grouped row p0 + m.
 // Returns M (rows of the expert) so callers can run epilogues.
-template <int KIND, int LK, int NB, bool PIPE>
+template <int KIND, int LK, int NB, bool PIPE, int NTHR = kThreads>
 __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
                                            const uint8_t* __restrict__ W,
                                            const uint16_t* __restrict__ S, int e, int tile,
@@ -121,8 +133,8 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
                                            int topk, int T, bool x_staged, uint32_t* xs,
                                            float* bsum, int* tok, const GemvStore& st) {
   constexpr int MAXM = kGemvMaxM;
-  constexpr int G = GemvGeom<KIND, LK>::G;
-  constexpr int UB = GemvGeom<KIND, LK>::UB;
+  constexpr int G = GemvGeom<KIND, LK, NTHR>::G;
+  constexpr int UB = GemvGeom<KIND, LK, NTHR>::UB;
   const int C = K / 32;     // 16-byte code chunks per row
   const int nch = C / LK;   // chunks per lane (uniform)
   const int units = N / 2;
@@ -195,7 +207,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
   for (int m0 = 0; m0 < M; m0 += MAXM) {
     const int Mc = min(MAXM, M - m0);
     if (KIND == 0) {
-      if (tid < Mc) tok[tid] = sorted[p0 + m0 + tid] / topk;
+      if (tid < Mc) tok[tid] = sorted[m0 + tid] / topk;
     } else {
       gemv_stage(A + static_cast<size_t>(p0 + m0) * K, Mc, K, xs, bsum);
     }
@@ -287,18 +299,23 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
   __shared__ int tok[kGemvMaxM];
   const int p0 = offsets[e];
   const int M = offsets[e + 1] - p0;
-  gemv_block<KIND, LK, NB, PIPE>(A, W, S, e, tile, p0, M, sorted_slot, K, N, topk, T, false, xs,
-                                 bsum, tok, GemvStore{out, N});
+  gemv_block<KIND, LK, NB, PIPE>(A, W, S, e, tile, p0, M, sorted_slot + p0, K, N, topk, T, false,
+                                 xs, bsum, tok, GemvStore{out, N});
 }
 
 // ----------------------------------------------------- fused decode layer ----
 // Whole layer for T <= 4 in two kernels (moe_layer_w4a16 at small T).
 //
-// decode_gateup_kernel: every block routes all T tokens itself (one wave per
-// token, the routing of moe_route_topk) and builds the permutation in LDS
-// (the stable counting sort of moe_permute), then runs its gate/up GEMV tile.
-// Block 0 writes the routing outputs and a compact per-expert record
-// {e, p0, M} for the second kernel.
+// decode_gateup_kernel: block a * tiles + tile serves routed slot a (token
+// a / k, pick a % k). Every block routes all T tokens itself (one wave per
+// token, the routing of moe_route_topk), so its expert e = ids[a] is known
+// right after the top-k and the weight stream starts there; the block of the
+// first slot that picked e runs all of e's rows, later slots with the same
+// expert exit. Where e's rows sit in grouped order (the stable counting sort
+// of moe_permute) follows from wave ballots over the R ids while the codes
+// are in flight. The last block writes the routing outputs, the permutation
+// and a compact per-expert record {e, p0, M} for the second kernel; it does
+// no GEMV work, so that bookkeeping stays off the weight stream's path.
 //
 // decode_down_kernel: a block owns a tile of NR output rows of H for every
 // active expert. Its lane groups walk the (expert, row pair) work items of the
@@ -311,38 +328,27 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
 constexpr int kDecodeBlocks = 256;   // target blocks of the down kernel
+constexpr int kDecodeGateupBlocks = 512;     // working blocks of the persistent gate/up (2 per CU)
+constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
 
-template <int LK, int NB, bool PIPE, int S>
-__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x,
-    const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
-    int k, int tiles, int* __restrict__ ids_out, float* __restrict__ w_out,
-    int* __restrict__ offsets_out, int* __restrict__ sorted_out, int* __restrict__ pos_out,
-    int* __restrict__ active_out, int* __restrict__ n_active_out, uint16_t* __restrict__ h,
-    int* __restrict__ rec) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* xs = lds;                                            // [T][H/2]
-  float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][H/32]
-  int* s_off = reinterpret_cast<int*>(bsum + T * (H / 32));      // [E + 1]: counts, then offsets
-  __shared__ int s_ids[kDecodeMaxR];
-  __shared__ float s_w[kDecodeMaxR];
-  __shared__ int s_sorted[kDecodeMaxR];
-  __shared__ int s_pos[kDecodeMaxR];
-  __shared__ int s_act[kDecodeMaxR];
-  __shared__ int s_tot[4];
-  __shared__ int tok[kGemvMaxM];
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int R = T * k;
-
-  // x rows do not depend on routing: stage them first
-  gemv_stage(x, T, H, xs, bsum);
-  for (int i = tid; i <= E; i += kThreads) s_off[i] = 0;
-  if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
+// Routing bookkeeping of the fused layer (the last gate/up block): counts,
+// exclusive offsets, active list, stable slot order; writes the routing
+// outputs and the per-expert records (entries past n_active repeat the last
+// active expert, so readers may index any slot below min(R, E)).
+template <int NTHR>
+__device__ __forceinline__ void decode_bookkeeping(const int* s_ids, const float* s_w, int* s_off,
+                                                   int* s_sorted, int* s_pos, int* s_act,
+                                                   int* s_tot, int R, int E, int* ids_out,
+                                                   float* w_out, int* offsets_out,
+                                                   int* sorted_out, int* pos_out, int* active_out,
+                                                   int* n_active_out, int* rec) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += NTHR) s_off[i] = 0;
   __syncthreads();
   if (tid < R) atomicAdd(&s_off[s_ids[tid]], 1);
   __syncthreads();
-  // counts -> exclusive offsets and the active list (E <= 1024: 4 per thread)
-  const int ept = (E + kThreads - 1) / kThreads;
+  // counts -> exclusive offsets and the active list (E <= 1024: <= 4 per thread)
+  const int ept = (E + NTHR - 1) / NTHR;
   int c[4], sc = 0, sf = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -352,8 +358,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
     sf += c[i] > 0;
   }
   int tot_c, na;
-  int oc = block256_excl_scan(sc, s_tot, tot_c);
-  int of = block256_excl_scan(sf, s_tot, na);
+  int oc = block_excl_scan<NTHR>(sc, s_tot, tot_c);
+  int of = block_excl_scan<NTHR>(sf, s_tot, na);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * ept + i;
@@ -376,34 +382,255 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
     s_pos[tid] = p;
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int i = tid; i < R; i += kThreads) {
-      ids_out[i] = s_ids[i];
-      w_out[i] = s_w[i];
-      sorted_out[i] = s_sorted[i];
-      pos_out[i] = s_pos[i];
-    }
-    for (int i = tid; i <= E; i += kThreads) offsets_out[i] = s_off[i];
-    for (int i = tid; i < na; i += kThreads) {
-      const int e = s_act[i];
-      active_out[i] = e;
-      rec[1 + 3 * i] = e;
-      rec[2 + 3 * i] = s_off[e];
-      rec[3 + 3 * i] = s_off[e + 1] - s_off[e];
-    }
-    if (tid == 0) {
-      *n_active_out = na;
-      rec[0] = na;
-    }
+  for (int i = tid; i < R; i += NTHR) {
+    ids_out[i] = s_ids[i];
+    w_out[i] = s_w[i];
+    sorted_out[i] = s_sorted[i];
+    pos_out[i] = s_pos[i];
   }
+  for (int i = tid; i <= E; i += NTHR) offsets_out[i] = s_off[i];
+  const int act = R < E ? R : E;
+  for (int i = tid; i < act; i += NTHR) {
+    const int e = s_act[i < na ? i : na - 1];
+    if (i < na) active_out[i] = e;
+    rec[1 + 3 * i] = e;
+    rec[2 + 3 * i] = s_off[e];
+    rec[3 + 3 * i] = s_off[e + 1] - s_off[e];
+  }
+  if (tid == 0) {
+    *n_active_out = na;
+    rec[0] = na;
+  }
+}
+
+// An empty use of loaded registers: the compiler waits for their loads here.
+__device__ __forceinline__ void use_regs(const uint4& a, const uint4& b, uint32_t c, uint32_t d) {
+  asm volatile("" ::"v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z),
+               "v"(b.w), "v"(c), "v"(d));
+}
+
+// One 16-byte chunk (32 codes) of a gate row and its up row against one staged
+// activation row (pair-permuted bf16 in LDS): raw dot products, before the
+// bias sum and the scale.
+__device__ __forceinline__ void dot_chunk2(const uint4& q0, const uint4& q1, const uint32_t* xrow,
+                                           int c, float& d0, float& d1) {
+  const uint4* xp = reinterpret_cast<const uint4*>(xrow + c * 16);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint4 xv = xp[v];
+    uint32_t w0 = (&q0.x)[v], w1 = (&q1.x)[v];
+    asm volatile("" : "+v"(w0), "+v"(w1));
+    uint32_t a0, a1, a2, a3;
+    nibble_pairs(w0, a0, a1, a2, a3);
+    d0 = dot2_bf16(a0, xv.x, d0);
+    d0 = dot2_bf16(a1, xv.y, d0);
+    d0 = dot2_bf16(a2, xv.z, d0);
+    d0 = dot2_bf16(a3, xv.w, d0);
+    nibble_pairs(w1, a0, a1, a2, a3);
+    d1 = dot2_bf16(a0, xv.x, d1);
+    d1 = dot2_bf16(a1, xv.y, d1);
+    d1 = dot2_bf16(a2, xv.z, d1);
+    d1 = dot2_bf16(a3, xv.w, d1);
+  }
+}
+
+// Slot-per-block gate/up of the fused decode layer, for small grids: block
+// a * tiles + tile serves routed slot a (token a / k, pick a % k) and one tile
+// of UB units. Its expert e = ids[a] is known right after the top-k, so the
+// weight stream starts there; the block of the first slot that picked e runs
+// all of e's rows, later slots with the same expert exit. Where e's rows sit
+// in grouped order follows from wave ballots over the R ids. The last block
+// does the bookkeeping, as in the persistent variant below.
+template <int LK, int NB, int S>
+__global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
+    int k, int tiles, int* __restrict__ ids_out, float* __restrict__ w_out,
+    int* __restrict__ offsets_out, int* __restrict__ sorted_out, int* __restrict__ pos_out,
+    int* __restrict__ active_out, int* __restrict__ n_active_out, uint16_t* __restrict__ h,
+    int* __restrict__ rec) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* xs = lds;                                            // [T][H/2]
+  float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][H/32]
+  int* s_off = reinterpret_cast<int*>(bsum + T * (H / 32));      // [E + 1] (bookkeeping)
+  __shared__ int s_ids[kDecodeMaxR];
+  __shared__ float s_w[kDecodeMaxR];
+  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR], s_tot[4];
+  __shared__ int tok[kGemvMaxM];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  const int R = T * k;
+
+  if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
+  if (blockIdx.x == gridDim.x - 1) {  // uniform: the bookkeeping block
+    __syncthreads();
+    decode_bookkeeping<kThreads>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
+                                 w_out, offsets_out, sorted_out, pos_out, active_out,
+                                 n_active_out, rec);
+    return;
+  }
+  gemv_stage(x, T, H, xs, bsum);
+  __syncthreads();
   const int a = blockIdx.x / tiles;
-  if (a >= na) return;  // uniform per block
   const int tile = blockIdx.x - a * tiles;
-  const int e = s_act[a];
-  const int p0 = s_off[e];
-  const int M = s_off[e + 1] - p0;
-  gemv_block<0, LK, NB, PIPE>(x, w13, s13, e, tile, p0, M, s_sorted, H, 2 * I, k, T, true, xs,
-                              bsum, tok, GemvStore{h, 2 * I});
+  const int e = s_ids[a];
+  // e's rows are the slots f with ids[f] == e, in increasing f; p0 = number of
+  // slots with a smaller expert id. Every wave forms the same ballots.
+  int p0 = 0, M = 0, earlier = 0;
+  for (int f0 = 0; f0 < R; f0 += kWave) {
+    const int f = f0 + lane;
+    const int id = f < R ? s_ids[f] : E;
+    const uint64_t eq = __ballot(id == e);
+    p0 += __popcll(__ballot(id < e));
+    const uint64_t below = a - f0 >= kWave ? ~0ull : (a - f0 <= 0 ? 0ull : (1ull << (a - f0)) - 1);
+    earlier += __popcll(eq & below);
+    if (wv == 0 && id == e) s_sorted[M + __popcll(eq & ((1ull << lane) - 1))] = f;
+    M += __popcll(eq);
+  }
+  if (earlier) return;  // uniform: an earlier slot's block runs expert e
+  // s_sorted[m] was written by wave 0, the only wave that reads it (tok fill)
+  gemv_block<0, LK, NB, false>(x, w13, s13, e, tile, p0, M, s_sorted, H, 2 * I, k, T, true, xs,
+                               bsum, tok, GemvStore{h, 2 * I});
+}
+
+// Persistent gate/up of the fused decode layer. Blocks 0..nblk-1 work, block
+// nblk does the bookkeeping. Every block routes the T tokens; each wave then
+// lists the active experts in order of first pick (expert, grouped offset,
+// rows, their tokens) from the R ids, all waves writing the same table. The
+// work is na * I units (an active expert's gate row u with its up row I + u);
+// lane group g of the grid takes units g, g + NGt, ... with the codes of two
+// units in flight, so every block streams an equal share whatever na is.
+// LK lanes split the H/32 code chunks of a row, NB = H/32/LK chunks each.
+template <int LK, int NB, int S>
+__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
+    int k, int* __restrict__ ids_out, float* __restrict__ w_out, int* __restrict__ offsets_out,
+    int* __restrict__ sorted_out, int* __restrict__ pos_out, int* __restrict__ active_out,
+    int* __restrict__ n_active_out, uint16_t* __restrict__ h, int* __restrict__ rec) {
+  constexpr int G = kWave / LK;                  // lane groups per wave
+  constexpr int NGB = (kThreads / kWave) * G;    // lane groups per block
+  extern __shared__ uint32_t lds[];
+  const int C = H / 32;                                          // 16-byte chunks per row
+  uint32_t* xs = lds;                                            // [T][H/2]
+  float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][C]
+  int* s_off = reinterpret_cast<int*>(bsum + T * C);             // [E + 1] (bookkeeping)
+  __shared__ int s_ids[kDecodeMaxR];
+  __shared__ float s_w[kDecodeMaxR];
+  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR], s_tot[4];
+  __shared__ int s_ae[kDecodeMaxR], s_ap0[kDecodeMaxR], s_am[kDecodeMaxR];
+  __shared__ int s_atok[kDecodeMaxR][kDecodeMaxT];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  const int R = T * k;
+  const int nblk = gridDim.x - 1;
+
+  if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
+  if (blockIdx.x == nblk) {  // uniform: the bookkeeping block
+    __syncthreads();
+    decode_bookkeeping<kThreads>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
+                                 w_out, offsets_out, sorted_out, pos_out, active_out,
+                                 n_active_out, rec);
+    return;
+  }
+  gemv_stage(x, T, H, xs, bsum);
+  __syncthreads();
+
+  // active experts in order of first pick; p0 = slots with a smaller id (the
+  // expert's first grouped row), tokens in slot order (a token picks an
+  // expert at most once, so an expert has at most T rows)
+  int na = 0;
+  const int id_lo = lane < R ? s_ids[lane] : -1;
+  const int id_hi = kWave + lane < R ? s_ids[kWave + lane] : -1;
+  for (int f0 = 0; f0 < R; f0 += kWave) {
+    const int f = f0 + lane;
+    const int id = f0 == 0 ? id_lo : id_hi;
+    int lt = 0, before = 0, mm = 0;
+    uint32_t toks = 0;  // 2 bits per row: tokens of this expert in slot order
+    for (int g = 0; g < R; ++g) {
+      const int ig = __builtin_amdgcn_readlane(g < kWave ? id_lo : id_hi, g & (kWave - 1));
+      lt += ig < id;
+      if (ig == id) {
+        before += g < f;
+        if (mm < kDecodeMaxT) toks |= static_cast<uint32_t>(g / k) << (2 * mm++);
+      }
+    }
+    const bool first = f < R && before == 0;
+    const uint64_t fm = __ballot(first);
+    if (first) {
+      const int a = na + __popcll(fm & ((1ull << lane) - 1));
+      for (int m = 0; m < mm; ++m) s_atok[a][m] = (toks >> (2 * m)) & 3;
+      s_ae[a] = id;
+      s_ap0[a] = lt;
+      s_am[a] = mm;
+    }
+    na += __popcll(fm);
+  }
+
+  const int U = na * I;
+  const size_t rowb = static_cast<size_t>(H / 2), srow = static_cast<size_t>(H / kGroup);
+  const int gid = blockIdx.x * NGB + wv * G + lane / LK, lk = lane % LK;
+  const int NGt = nblk * NGB;
+  // codes and raw fp16 scales of one unit; the scales stay unpacked so that
+  // nothing waits on a load until the unit is computed
+  struct Unit {
+    uint4 q0[NB], q1[NB];
+    uint32_t s0[NB], s1[NB];
+  };
+  Unit ua, ub;
+  auto load_unit = [&](int q, Unit& w) {
+    q = min(q, U - 1);
+    const int a = q / I, u = q - a * I;
+    const size_t r0 = static_cast<size_t>(s_ae[a]) * (2 * I) + u;
+    const uint8_t* W0 = w13 + r0 * rowb + lk * 16;
+    const uint16_t* S0 = s13 + r0 * srow;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      w.q0[b] = ld16(W0 + b * LK * 16);
+      w.q1[b] = ld16(W0 + I * rowb + b * LK * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = lk + b * LK;
+      w.s0[b] = S0[c >> 2];
+      w.s1[b] = S0[I * srow + (c >> 2)];
+    }
+  };
+  auto run_unit = [&](int q, const Unit& w) {
+    // wait for exactly this unit's loads here, in straight-line code, so the
+    // row loop below does not drain the other unit's loads as well
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      use_regs(w.q0[b], w.q1[b], w.s0[b], w.s1[b]);
+    const int a = q / I, u = q - a * I;
+    const int p0 = s_ap0[a], M = s_am[a];
+    for (int m = 0; m < M; ++m) {
+      const int t = s_atok[a][m];
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = lk + b * LK;
+        float d0 = 0.0f, d1 = 0.0f;
+        dot_chunk2(w.q0[b], w.q1[b], xs + t * (H / 2), c, d0, d1);
+        const float cs = bsum[t * C + c];
+        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(w.s0[b])) * (d0 - cs);
+        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(w.s1[b])) * (d1 - cs);
+      }
+#pragma unroll
+      for (int sh = LK / 2; sh >= 1; sh >>= 1) {
+        acc0 += wave_shfl_xor(acc0, sh);
+        acc1 += wave_shfl_xor(acc1, sh);
+      }
+      if (lk == 0) h[static_cast<size_t>(p0 + m) * I + u] = f32_to_bf16(silu_mul(acc0, acc1));
+    }
+  };
+  // units gid, gid + NGt, ...: two register sets alternate
+  load_unit(gid, ua);
+  load_unit(gid + NGt, ub);
+  for (int q = gid; q < U; q += 2 * NGt) {
+    run_unit(q, ua);
+    if (q + 2 * NGt < U) load_unit(q + 2 * NGt, ua);
+    if (q + NGt < U) run_unit(q + NGt, ub);
+    if (q + 3 * NGt < U) load_unit(q + 3 * NGt, ub);
+  }
 }
 
 // NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
@@ -411,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
 template <int LK, int NB>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
-    const uint16_t* __restrict__ s2, int T, int H, int I, int k, int upb,
+    const uint16_t* __restrict__ s2, int T, int H, int I, int E, int k, int upb,
     const int* __restrict__ rec, const int* __restrict__ slot_pos,
     const float* __restrict__ topk_w, float* __restrict__ y, float* __restrict__ out) {
   constexpr int G = kWave / LK;       // lane groups per wave
@@ -429,7 +656,42 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   const int u0 = blockIdx.x * upb;                 // first unit (row pair) of the tile
   const int units = H / 2;
 
+  // work item q = (active expert a, unit uu of the tile): two W2 rows; codes
+  // and raw fp16 scales stay unpacked so nothing waits on a load early
+  const size_t rowb = static_cast<size_t>(I / 2), srow = static_cast<size_t>(I / kGroup);
+  struct Item {
+    uint4 q0[NB], q1[NB];
+    uint32_t s0[NB], s1[NB];
+  };
+  Item ia, ib;
+  auto load_codes = [&](int e, int u, Item& w) {
+    const uint8_t* W0 = w2 + (static_cast<size_t>(e) * H + 2 * u) * rowb + lk * 16;
+    const uint16_t* S0 = s2 + (static_cast<size_t>(e) * H + 2 * u) * srow;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      w.q0[b] = ld16(W0 + b * LK * 16);
+      w.q1[b] = ld16(W0 + rowb + b * LK * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = lk + b * LK;
+      w.s0[b] = S0[c >> 2];
+      w.s1[b] = S0[srow + (c >> 2)];
+    }
+  };
+  // The first two items' codes go out before anything else: their expert is
+  // read straight from the record (slot clamped below min(R, E), id clamped to
+  // [0, E): every record slot holds a valid expert, the clamps only keep the
+  // address in bounds), alongside the count of active experts.
+  const int act = R < E ? R : E;
   const int na = rec[0];
+  auto first_codes = [&](int q, Item& w) {
+    const int a = min(q / upb, act - 1);
+    const int e = min(max(rec[1 + 3 * a], 0), E - 1);
+    load_codes(e, min(u0 + (q - (q / upb) * upb), units - 1), w);
+  };
+  first_codes(lg, ia);
+  first_codes(lg + NG, ib);
   for (int i = tid; i < na; i += kThreads) {
     s_e[i] = rec[1 + 3 * i];
     s_p0[i] = rec[2 + 3 * i];
@@ -437,36 +699,17 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   }
   gemv_stage(h, R, I, xs, bsum);
   __syncthreads();
-
-  // work item q = (active expert a, unit uu of the tile)
   const int nitems = na * upb;
-  const size_t rowb = static_cast<size_t>(I / 2), srow = static_cast<size_t>(I / kGroup);
-  auto item_rows = [&](int q, int& e, int& u) {
-    const int a = q / upb;
-    const int uu = q - a * upb;
-    e = s_e[a];
-    u = min(u0 + uu, units - 1);
+  auto load_item = [&](int q, Item& w) {
+    const int qq = min(q, nitems - 1);
+    const int a = qq / upb;
+    load_codes(s_e[a], min(u0 + (qq - a * upb), units - 1), w);
   };
-  uint4 qa0[NB], qa1[NB], qb0[NB], qb1[NB];
-  uint32_t sa[NB], sb[NB];
-  auto load_item = [&](int q, uint4 (&q0)[NB], uint4 (&q1)[NB], uint32_t (&sc)[NB]) {
-    int e, u;
-    item_rows(min(q, nitems - 1), e, u);
-    const uint8_t* W0 = w2 + (static_cast<size_t>(e) * H + 2 * u) * rowb + lk * 16;
-    const uint16_t* S0 = s2 + (static_cast<size_t>(e) * H + 2 * u) * srow;
+  auto run_item = [&](int q, const Item& w) {
+    // wait for exactly this item's loads here, in straight-line code
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      q0[b] = ld16(W0 + b * LK * 16);
-      q1[b] = ld16(W0 + rowb + b * LK * 16);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int c = lk + b * LK;
-      sc[b] = static_cast<uint32_t>(S0[c >> 2]) | (static_cast<uint32_t>(S0[srow + (c >> 2)]) << 16);
-    }
-  };
-  auto run_item = [&](int q, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
-                      const uint32_t (&sc)[NB]) {
+    for (int b = 0; b < NB; ++b)
+      use_regs(w.q0[b], w.q1[b], w.s0[b], w.s1[b]);
     const int a = q / upb;
     const int uu = q - a * upb;
     const int p0 = s_p0[a], M = s_m[a];
@@ -477,28 +720,11 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int c = lk + b * LK;
-        const uint4* xp = reinterpret_cast<const uint4*>(xs + xr * (I / 2) + c * 16);
         float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 xv = xp[v];
-          uint32_t c0 = (&q0[b].x)[v], c1 = (&q1[b].x)[v];
-          asm volatile("" : "+v"(c0), "+v"(c1));
-          uint32_t a0, a1, a2, a3;
-          nibble_pairs(c0, a0, a1, a2, a3);
-          d0 = dot2_bf16(a0, xv.x, d0);
-          d0 = dot2_bf16(a1, xv.y, d0);
-          d0 = dot2_bf16(a2, xv.z, d0);
-          d0 = dot2_bf16(a3, xv.w, d0);
-          nibble_pairs(c1, a0, a1, a2, a3);
-          d1 = dot2_bf16(a0, xv.x, d1);
-          d1 = dot2_bf16(a1, xv.y, d1);
-          d1 = dot2_bf16(a2, xv.z, d1);
-          d1 = dot2_bf16(a3, xv.w, d1);
-        }
+        dot_chunk2(w.q0[b], w.q1[b], xs + xr * (I / 2), c, d0, d1);
         const float cs = bsum[xr * C + c];
-        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu)) * (d0 - cs);
-        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16)) * (d1 - cs);
+        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(w.s0[b])) * (d0 - cs);
+        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(w.s1[b])) * (d1 - cs);
       }
 #pragma unroll
       for (int sh = LK / 2; sh >= 1; sh >>= 1) {
@@ -514,13 +740,13 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     }
   };
   // items lg, lg + NG, ...: two register sets alternate so the next item's
-  // codes stream while the current one is computed
-  if (lg < nitems) load_item(lg, qa0, qa1, sa);
+  // codes stream while the current one is computed (items lg and lg + NG are
+  // already in flight)
   for (int q = lg; q < nitems; q += 2 * NG) {
-    if (q + NG < nitems) load_item(q + NG, qb0, qb1, sb);
-    run_item(q, qa0, qa1, sa);
-    if (q + 2 * NG < nitems) load_item(q + 2 * NG, qa0, qa1, sa);
-    if (q + NG < nitems) run_item(q + NG, qb0, qb1, sb);
+    run_item(q, ia);
+    if (q + 2 * NG < nitems) load_item(q + 2 * NG, ia);
+    if (q + NG < nitems) run_item(q + NG, ib);
+    if (q + 3 * NG < nitems) load_item(q + 3 * NG, ib);
   }
   __syncthreads();
   // combine for this tile's rows, in increasing j
@@ -604,31 +830,94 @@ hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                                     N, topk, max_active, T, s);
 }
 
-template <int LK, int NB, bool PIPE>
-struct DecodeGateupLaunch {
-  static hipError_t run(const float* logits, const uint16_t* x, const uint8_t* w13,
-                        const uint16_t* s13, int T, int H, int I, int E, int k, int* ids, float* w,
-                        int* offsets, int* sorted_slot, int* slot_pos, int* active, int* n_active,
-                        uint16_t* h, int* rec, int max_active, hipStream_t s) {
-    constexpr int UB = GemvGeom<0, LK>::UB;
-    const int tiles = (I + UB - 1) / UB;
-    const size_t lds = gemv_lds_bytes(T, H) + static_cast<size_t>(E + 1) * 4;
+// Lane split of the fused gate/up: the smallest LK in {8, 16, 32} dividing the
+// H/32 code chunks of a row with at most 4 chunks per lane, else at most 8;
+// 0 if none.
+inline int decode_gateup_lk(int H) {
+  const int C = H / 32;
+  for (int cap = 4; cap <= 8; cap *= 2)
+    for (int lk = 8; lk <= 32; lk *= 2)
+      if (C % lk == 0 && C / lk <= cap) return lk;
+  return 0;
+}
+
+template <int LK, int NB>
+hipError_t launch_decode_gateup_t(const float* logits, const uint16_t* x, const uint8_t* w13,
+                                  const uint16_t* s13, int T, int H, int I, int E, int k, int* ids,
+                                  float* w, int* offsets, int* sorted_slot, int* slot_pos,
+                                  int* active, int* n_active, uint16_t* h, int* rec,
+                                  hipStream_t s) {
+  const size_t lds = gemv_lds_bytes(T, H) + static_cast<size_t>(E + 1) * 4;
+  auto attr = [&](const void* kern) -> hipError_t {
+    if (lds <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(lds));
+  };
+  // slot-per-block while its grid stays within a few blocks per CU (one unit
+  // per lane group, all codes in registers); persistent otherwise. Both add
+  // the bookkeeping block.
+  constexpr int UB = GemvGeom<0, LK>::UB;
+  const int tiles = (I + UB - 1) / UB;
+  const long long slot_blocks = static_cast<long long>(T) * k * tiles;
+  if (NB <= 4 && slot_blocks <= kDecodeSlotMaxBlocks) {
     auto go = [&](auto kern) -> hipError_t {
-      if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-      }
-      hipLaunchKernelGGL(kern, dim3(max_active * tiles), dim3(kThreads), lds, s, logits, x, w13,
-                         s13, T, H, I, E, k, tiles, ids, w, offsets, sorted_slot, slot_pos,
-                         active, n_active, h, rec);
+      const hipError_t e = attr(reinterpret_cast<const void*>(kern));
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slot_blocks) + 1), dim3(kThreads), lds,
+                         s, logits, x, w13, s13, T, H, I, E, k, tiles, ids, w, offsets,
+                         sorted_slot, slot_pos, active, n_active, h, rec);
       return hipGetLastError();
     };
-    if (E <= 256) return go(&decode_gateup_kernel<LK, NB, PIPE, 4>);
-    return go(&decode_gateup_kernel<LK, NB, PIPE, 16>);
+    constexpr int NBS = NB <= 4 ? NB : 4;
+    if (E <= 128) return go(&decode_gateup_slot_kernel<LK, NBS, 2>);
+    if (E <= 256) return go(&decode_gateup_slot_kernel<LK, NBS, 4>);
+    return go(&decode_gateup_slot_kernel<LK, NBS, 16>);
   }
-};
+  auto go = [&](auto kern) -> hipError_t {
+    const hipError_t e = attr(reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(kDecodeGateupBlocks + 1), dim3(kThreads), lds, s, logits, x,
+                       w13, s13, T, H, I, E, k, ids, w, offsets, sorted_slot, slot_pos, active,
+                       n_active, h, rec);
+    return hipGetLastError();
+  };
+  if (E <= 128) return go(&decode_gateup_kernel<LK, NB, 2>);
+  if (E <= 256) return go(&decode_gateup_kernel<LK, NB, 4>);
+  return go(&decode_gateup_kernel<LK, NB, 16>);
+}
+
+template <int LK, typename... Args>
+hipError_t decode_gateup_nb(int nb, Args... args) {
+  switch (nb) {
+    case 1: return launch_decode_gateup_t<LK, 1>(args...);
+    case 2: return launch_decode_gateup_t<LK, 2>(args...);
+    case 3: return launch_decode_gateup_t<LK, 3>(args...);
+    case 4: return launch_decode_gateup_t<LK, 4>(args...);
+    case 5: return launch_decode_gateup_t<LK, 5>(args...);
+    case 6: return launch_decode_gateup_t<LK, 6>(args...);
+    case 7: return launch_decode_gateup_t<LK, 7>(args...);
+    case 8: return launch_decode_gateup_t<LK, 8>(args...);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_gateup(const float* logits, const uint16_t* x, const uint8_t* w13,
+                                const uint16_t* s13, int T, int H, int I, int E, int k, int* ids,
+                                float* w, int* offsets, int* sorted_slot, int* slot_pos,
+                                int* active, int* n_active, uint16_t* h, int* rec, hipStream_t s) {
+  const int lk = decode_gateup_lk(H);
+  const int nb = lk ? H / 32 / lk : 0;
+  if (lk == 8)
+    return decode_gateup_nb<8>(nb, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
+                               sorted_slot, slot_pos, active, n_active, h, rec, s);
+  if (lk == 16)
+    return decode_gateup_nb<16>(nb, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
+                                sorted_slot, slot_pos, active, n_active, h, rec, s);
+  if (lk == 32)
+    return decode_gateup_nb<32>(nb, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
+                                sorted_slot, slot_pos, active, n_active, h, rec, s);
+  return hipErrorInvalidValue;
+}
 
 // Down tile size: enough units per block for about kDecodeBlocks blocks.
 inline int decode_down_upb(int H) { return (H / 2 + kDecodeBlocks - 1) / kDecodeBlocks; }
@@ -641,7 +930,7 @@ inline size_t decode_down_lds(int T, int H, int I, int k) {
 template <int LK, int NB, bool PIPE>
 struct DecodeDownLaunch {
   static hipError_t run(const uint16_t* h, const uint8_t* w2, const uint16_t* s2, int T, int H,
-                        int I, int k, const int* rec, const int* slot_pos, const float* w,
+                        int I, int E, int k, const int* rec, const int* slot_pos, const float* w,
                         float* y, float* out, hipStream_t s) {
     if (PIPE) return hipErrorInvalidValue;  // excluded by the host dispatch rule
     const int upb = decode_down_upb(H);
@@ -654,8 +943,8 @@ struct DecodeDownLaunch {
                                                static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, k, upb, rec,
-                       slot_pos, w, y, out);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, E, k, upb,
+                       rec, slot_pos, w, y, out);
     return hipGetLastError();
   }
 };
@@ -928,7 +1217,7 @@ LayerWs layer_carve(void* ws, int T, int I, int E, int k) {
 // The two-kernel decode layer: T <= 4, the down kernel's codes fit one
 // register batch (I / 32 / LK <= 4) and its staged h rows fit LDS.
 bool layer_fused(int T, int H, int I, int k) {
-  if (T > kDecodeMaxT || T * k > kDecodeMaxR) return false;
+  if (T > kDecodeMaxT || T * k > kDecodeMaxR || decode_gateup_lk(H) == 0) return false;
   const int C = I / 32;
   const int LK = (C % 16 == 0 && C >= 64) ? 16 : (C % 8 == 0 ? 8 : 4);
   if (C / LK > 4) return false;
@@ -950,14 +1239,12 @@ hipError_t launch_w4a16_layer(int T, int H, int I, int E, int k, const float* lo
                               int* n_active, float* y, float* out, void* ws, hipStream_t s) {
   const LayerWs lw = layer_carve(ws, T, I, E, k);
   if (T > 0 && layer_fused(T, H, I, k)) {
-    const int R = T * k;
-    const int max_active = R < E ? R : E;
-    hipError_t err = gemv_dispatch<DecodeGateupLaunch>(
-        H, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets, sorted_slot, slot_pos, active,
-        n_active, lw.h, lw.rec, max_active, s);
+    hipError_t err = launch_decode_gateup(logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
+                                          sorted_slot, slot_pos, active, n_active, lw.h, lw.rec,
+                                          s);
     if (err != hipSuccess) return err;
-    return gemv_dispatch<DecodeDownLaunch>(I, lw.h, w2, s2, T, H, I, k, lw.rec, slot_pos, w, y,
-                                           out, s);
+    return gemv_dispatch<DecodeDownLaunch>(I, lw.h, w2, s2, T, H, I, E, k, lw.rec, slot_pos, w,
+                                           y, out, s);
   }
   hipError_t err = launch_route_topk(logits, T, E, k, ids, w, s);
   if (err != hipSuccess) return err;
