@@ -55,6 +55,26 @@ __device__ __forceinline__ void nibble_pairs(uint32_t w, uint32_t& p0, uint32_t&
   p2 = ((w >> 8) & kMask) | kHi;
   p3 = ((w >> 12) & kMask) | kHi;
 }
+// The two constants of nibble_pairs() as register values: VOP3 takes no
+// literal on gfx9, so with both constants folded the compiler splits every
+// and-or into two instructions; held in registers, each is one v_and_or_b32.
+// Create once per kernel (outside loops) and pass to nibble_pairs_r().
+struct NibbleConsts {
+  uint32_t mask, hi;
+};
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+  NibbleConsts k;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.mask));
+  asm volatile("s_mov_b32 %0, 0x43004300" : "=s"(k.hi));
+  return k;
+}
+__device__ __forceinline__ void nibble_pairs_r(uint32_t w, const NibbleConsts& k, uint32_t& p0,
+                                               uint32_t& p1, uint32_t& p2, uint32_t& p3) {
+  p0 = (w & k.mask) | k.hi;
+  p1 = ((w >> 4) & k.mask) | k.hi;
+  p2 = ((w >> 8) & k.mask) | k.hi;
+  p3 = ((w >> 12) & k.mask) | k.hi;
+}
 // bf16 pair (136, 136): 128 (bf16 exponent trick) + 8 (zero point); the codes
 // of a zero weight widen to exactly this pattern.
 constexpr uint32_t kBiasPair = 0x43084308u;

@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int* __res
 }
 
 // One block: column prefix sums over chunks, expert offsets, active list.
+// bases[b][e] = rows of expert e in chunks before b (within-expert prefix);
+// the scatter adds the expert's offset. Loads go out eight at a time.
 __global__ __launch_bounds__(kThreads) void permute_scan_kernel(
     const int* __restrict__ hist, int* __restrict__ bases, int NB, int R, int E,
     int* __restrict__ offsets, int* __restrict__ active, int* __restrict__ n_active) {
@@ -185,8 +187,18 @@ __global__ __launch_bounds__(kThreads) void permute_scan_kernel(
   int* run = sm + E;      // [E]
   __shared__ int wave_tot[kWaves];
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    int acc = 0;
-    for (int b = 0; b < NB; ++b) {
+    int acc = 0, b = 0;
+    for (; b + 8 <= NB; b += 8) {
+      int hv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hv[u] = hist[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        bases[static_cast<size_t>(b + u) * E + e] = acc;
+        acc += hv[u];
+      }
+    }
+    for (; b < NB; ++b) {
       const size_t i = static_cast<size_t>(b) * E + e;
       const int h = hist[i];
       bases[i] = acc;
@@ -196,21 +208,17 @@ __global__ __launch_bounds__(kThreads) void permute_scan_kernel(
   }
   __syncthreads();
   offsets_and_active(counts, run, E, R, wave_tot, offsets, active, n_active);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int off = run[e];
-    for (int b = 0; b < NB; ++b) bases[static_cast<size_t>(b) * E + e] += off;
-  }
 }
 
 __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
-    const int* __restrict__ ids, const int* __restrict__ bases, int R, int E,
-    int* __restrict__ sorted_slot, int* __restrict__ slot_pos) {
+    const int* __restrict__ ids, const int* __restrict__ bases,
+    const int* __restrict__ offsets, int R, int E, int* __restrict__ sorted_slot,
+    int* __restrict__ slot_pos) {
   extern __shared__ int sm[];
   int* run = sm;          // [E]
   int* wc = sm + E;       // [kWaves * E]
   for (int e = threadIdx.x; e < E; e += kThreads)
-    run[e] = bases[static_cast<size_t>(blockIdx.x) * E + e];
+    run[e] = offsets[e] + bases[static_cast<size_t>(blockIdx.x) * E + e];
   for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wc[i] = 0;
   __syncthreads();
   scatter_chunk(ids, R, E, id_bits(E), blockIdx.x * kChunk, run, wc, sorted_slot, slot_pos);
@@ -241,7 +249,7 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* offsets, int
   permute_scan_kernel<<<1, kThreads, 2 * E * sizeof(int), s>>>(hist, bases, NB, R, E, offsets,
                                                                active, n_active);
   permute_scatter_kernel<<<NB, kThreads, (1 + kWaves) * E * sizeof(int), s>>>(
-      ids, bases, R, E, sorted_slot, slot_pos);
+      ids, bases, offsets, R, E, sorted_slot, slot_pos);
   return hipGetLastError();
 }
 

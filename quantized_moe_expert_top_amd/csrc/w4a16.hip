@@ -634,8 +634,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
 }
 
 // NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
-// separate calls).
-template <int LK, int NB>
+// separate calls). D: work items in flight per lane group.
+template <int LK, int NB, int D>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
     const uint16_t* __restrict__ s2, int T, int H, int I, int E, int k, int upb,
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     uint4 q0[NB], q1[NB];
     uint32_t s0[NB], s1[NB];
   };
-  Item ia, ib;
+  Item it[D];
   auto load_codes = [&](int e, int u, Item& w) {
     const uint8_t* W0 = w2 + (static_cast<size_t>(e) * H + 2 * u) * rowb + lk * 16;
     const uint16_t* S0 = s2 + (static_cast<size_t>(e) * H + 2 * u) * srow;
@@ -690,8 +690,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const int e = min(max(rec[1 + 3 * a], 0), E - 1);
     load_codes(e, min(u0 + (q - (q / upb) * upb), units - 1), w);
   };
-  first_codes(lg, ia);
-  first_codes(lg + NG, ib);
+#pragma unroll
+  for (int d = 0; d < D; ++d) first_codes(lg + d * NG, it[d]);
   for (int i = tid; i < na; i += kThreads) {
     s_e[i] = rec[1 + 3 * i];
     s_p0[i] = rec[2 + 3 * i];
@@ -739,14 +739,17 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
       }
     }
   };
-  // items lg, lg + NG, ...: two register sets alternate so the next item's
-  // codes stream while the current one is computed (items lg and lg + NG are
-  // already in flight)
-  for (int q = lg; q < nitems; q += 2 * NG) {
-    run_item(q, ia);
-    if (q + 2 * NG < nitems) load_item(q + 2 * NG, ia);
-    if (q + NG < nitems) run_item(q + NG, ib);
-    if (q + 3 * NG < nitems) load_item(q + 3 * NG, ib);
+  // items lg, lg + NG, ...: D register sets rotate so D - 1 items stream
+  // while one is computed (the first D are already in flight)
+  for (int q = lg; q < nitems; q += D * NG) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int qq = q + d * NG;
+      if (qq < nitems) {
+        run_item(qq, it[d]);
+        if (qq + D * NG < nitems) load_item(qq + D * NG, it[d]);
+      }
+    }
   }
   __syncthreads();
   // combine for this tile's rows, in increasing j
@@ -936,37 +939,56 @@ struct DecodeDownLaunch {
     const int upb = decode_down_upb(H);
     const int blocks = (H / 2 + upb - 1) / upb;
     const size_t lds = decode_down_lds(T, H, I, k);
-    auto kern = &decode_down_kernel<LK, (NB < 1 ? 1 : NB)>;
-    if (lds > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, E, k, upb,
-                       rec, slot_pos, w, y, out);
-    return hipGetLastError();
+    // items per lane group: (active experts) * upb / groups; deeper rings for
+    // tiles that hold many items
+    constexpr int NG = 4 * (kWave / LK);
+    const int items = (T * k < E ? T * k : E) * upb;
+    auto go = [&](auto kern) -> hipError_t {
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, E, k,
+                         upb, rec, slot_pos, w, y, out);
+      return hipGetLastError();
+    };
+    if (items > 4 * NG) return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 4>);
+    return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 2>);
   }
 };
 
 // ---------------------------------------------------------------- MFMA ----
-constexpr int kALd = kGroup + 8;  // LDS row stride of the activation tile (bf16)
-
 // KIND 0: gate/up. Wave w owns h-columns [nt*128 + 32w, +32): B subtile 0 is
 //         gate rows, subtile 1 the matching up rows.
 // KIND 1: down. Wave w owns W2 rows [nt*256 + 64w, +64) as two subtiles.
-// Operand k order: within each 16-k MFMA step, lane half hf = lane/32 takes
-// k = 64*hf + 8*s + {0,4,1,5,2,6,3,7} (s = step); A is stored in LDS in that
-// pair order, B comes out of nibble_pairs() in it.
+// K advances one scale group (128 k) per step with kMfD groups in flight:
+// each step requests group g + kMfD - 1 into a register ring of kMfD groups
+// per lane (the B codes and raw fp16 scales, and this thread's share of the
+// activation tile), computes group g, then writes group g + 1's activations,
+// pair-permuted, into its LDS stage. The LDS tile slot L of a stage holds row
+// L/16, 16-byte chunk (L%16) ^ (row%16), so the 32 rows an MFMA operand read
+// touches land in distinct banks.
+// Operand k order: within each 16-k MFMA step s, lane half hf = lane/32 takes
+// k = 64*hf + 8*s + {0,4,1,5,2,6,3,7}: B comes out of nibble_pairs() in that
+// order and A is stored in it.
+// Each group's MFMA partial sums on 128 + q are un-biased by the same MFMA
+// chain run on the constant 136 (= 128 + zero point), then scaled: all-8
+// codes give exactly zero.
+constexpr int kMfD = 3;  // groups in flight
+
 template <int KIND, int MT>
-__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
+__global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const uint16_t* __restrict__ S, const int* __restrict__ offsets,
-    const int* __restrict__ sorted_slot, void* __restrict__ out, int K, int N, int E,
-    int topk, int NT) {
+    const int* __restrict__ sorted_slot, void* __restrict__ out, int K, int N, int E, int topk,
+    int NT) {
   constexpr int BM = 32 * MT;
-  constexpr int CPT = BM * 16 / kThreads;  // 16-byte A chunks per thread per group
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * kALd];
+  constexpr int CPT = BM * 16 / kThreads;   // activation chunks per thread per group
+  constexpr int STAGE = BM * 16 * 16;       // bytes of one activation stage
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kMfD * STAGE];
+  __shared__ int row_src[BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[3];
 
@@ -976,7 +998,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int G = K / kGroup;
-  const size_t rowb = static_cast<size_t>(K / 2);
+
+  // source row of each tile row; rows past the expert's block read the first
+  // row (their results are dropped)
+  if (tid < BM) {
+    const int p = ti.p_begin + tid;
+    const int pv = p < ti.p_end ? p : ti.p_begin;
+    row_src[tid] = (KIND == 0) ? sorted_slot[pv] / topk : pv;
+  }
 
   // B rows of this lane (two subtiles)
   int nrow[2];
@@ -995,49 +1024,63 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
       nrow[j] = nvalid[j] ? n : N - 1;
     }
   }
-  const uint8_t* Wr[2];
-  const uint16_t* Sr[2];
+  // codes and scales of this expert through buffer resources: per-lane row
+  // offsets stay fixed, the group advances a scalar offset
+  const uint32_t rowb = static_cast<uint32_t>(K / 2);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      buffer_rsrc(W + static_cast<size_t>(ti.e) * N * rowb, static_cast<uint32_t>(N) * rowb);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      buffer_rsrc(S + static_cast<size_t>(ti.e) * N * G, static_cast<uint32_t>(N * G) * 2u);
+  uint32_t woff[2], soff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    Wr[j] = W + (static_cast<size_t>(ti.e) * N + nrow[j]) * rowb + hf * 32;
-    Sr[j] = S + (static_cast<size_t>(ti.e) * N + nrow[j]) * G;
+    woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
+    soff[j] = static_cast<uint32_t>(nrow[j] * G) * 2u;
   }
+  __syncthreads();
 
-  // A rows staged by this thread: chunk q = tid + 256*v -> row q/16, chunk q%16
-  const uint16_t* arow[CPT];
+  // this thread's activation chunks: slot L = tid + 256 v of a stage
+  const uint16_t* asrc[CPT];
+  int adst[CPT];
 #pragma unroll
   for (int v = 0; v < CPT; ++v) {
-    const int q = tid + kThreads * v;
-    const int r = q >> 4, ch = q & 15;
-    const int p = ti.p_begin + r;
-    if (p < ti.p_end) {
-      const size_t src = (KIND == 0) ? static_cast<size_t>(sorted_slot[p] / topk) : static_cast<size_t>(p);
-      arow[v] = A + src * K + ch * 8;
-    } else {
-      arow[v] = nullptr;
-    }
+    const int L = tid + kThreads * v, row = L >> 4, c = (L & 15) ^ (row & 15);
+    asrc[v] = A + static_cast<size_t>(row_src[row]) * K + c * 8;
+    adst[v] = L * 16;
+  }
+  // LDS offsets of this lane's A operand for the 8 MFMA steps of a group
+  int aoffs[MT][8];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = i * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) aoffs[i][s] = (row * 16 + ((hf * 8 + s) ^ (row & 15))) * 16;
   }
 
-  auto load_a = [&](int g, uint4* regs) {
-#pragma unroll
-    for (int v = 0; v < CPT; ++v)
-      regs[v] = arow[v] ? ld16(arow[v] + g * kGroup) : make_uint4(0, 0, 0, 0);
+  struct Grp {
+    uint4 q[2][2];
+    uint32_t sc[2];
+    uint4 a[CPT];
   };
-  auto store_a = [&](int buf, const uint4* regs) {
-#pragma unroll
-    for (int v = 0; v < CPT; ++v) {
-      const int q = tid + kThreads * v;
-      const int r = q >> 4, ch = q & 15;
-      *reinterpret_cast<uint4*>(&a_lds[buf][r * kALd + ch * 8]) = pair_permute(regs[v]);
-    }
-  };
-  auto load_b = [&](int g, uint4 (&bq)[2][2], float (&bs)[2]) {
+  Grp ring[kMfD];
+  auto issue = [&](int g, Grp& b) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      bq[j][0] = ld16(Wr[j] + g * 64);
-      bq[j][1] = ld16(Wr[j] + g * 64 + 16);
-      bs[j] = fp16_bits_to_f32(Sr[j][g]);
+      b.q[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                w_rsrc, woff[j], g * 64, 0));
+      b.q[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                w_rsrc, woff[j] + 16, g * 64, 0));
     }
+#pragma unroll
+    for (int v = 0; v < CPT; ++v) b.a[v] = ld16(asrc[v] + g * kGroup);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, soff[j], g * 2, 0);
+  };
+  auto stage_a = [&](const Grp& b, int stage) {
+#pragma unroll
+    for (int v = 0; v < CPT; ++v)
+      *reinterpret_cast<uint4*>(a_lds + stage * STAGE + adst[v]) = pair_permute(b.a[v]);
   };
 
   f32x16_t acc[MT][2];
@@ -1047,24 +1090,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const bf16x8_t bias_op =
+      __builtin_bit_cast(bf16x8_t, make_uint4(kBiasPair, kBiasPair, kBiasPair, kBiasPair));
 
-  uint4 areg[CPT];
-  uint4 bq[2][2], bq_next[2][2];
-  float bs[2], bs_next[2];
-  load_a(0, areg);
-  store_a(0, areg);
-  load_b(0, bq, bs);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (more) {
-      load_a(g + 1, areg);
-      load_b(g + 1, bq_next, bs_next);
-    }
-    // accg: the group's partial sums on 128 + q; cg: the same MFMA chain on
-    // constant 136 (= 128 + zero point), i.e. its exact bias term
+  const NibbleConsts nk = nibble_consts();
+  auto compute = [&](const Grp& b, int stage) {
+    const uint8_t* st = a_lds + stage * STAGE;
     f32x16_t accg[MT][2], cg[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -1075,46 +1106,60 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) accg[i][j][r] = 0.0f;
     }
-    const bf16x8_t bias_op = __builtin_bit_cast(
-        bf16x8_t, make_uint4(kBiasPair, kBiasPair, kBiasPair, kBiasPair));
+    // the group's A operands first, so their LDS latency overlaps the MFMAs
+    uint4 av[MT][8];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) av[i][s] = *reinterpret_cast<const uint4*>(st + aoffs[i][s]);
+    __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the unpack and MFMAs
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8_t bop[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t w = (&bq[j][s >> 2].x)[s & 3];
-        uint4 p;
-        nibble_pairs(w, p.x, p.y, p.z, p.w);
-        bop[j] = __builtin_bit_cast(bf16x8_t, p);
+        const uint32_t w = (&b.q[j][s >> 2].x)[s & 3];
+        uint4 pq;
+        nibble_pairs_r(w, nk, pq.x, pq.y, pq.z, pq.w);
+        bop[j] = __builtin_bit_cast(bf16x8_t, pq);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint4 av = *reinterpret_cast<const uint4*>(
-            &a_lds[buf][(i * 32 + l32) * kALd + hf * 64 + s * 8]);
-        const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
+        const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av[i][s]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[j], accg[i][j], 0, 0, 0);
         cg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bias_op, cg[i], 0, 0, 0);
       }
     }
-    // un-bias and scale the group's partial sums
+    float bs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bs[j] = fp16_bits_to_f32(static_cast<uint16_t>(b.sc[j]));
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += bs[j] * (accg[i][j][r] - cg[i][r]);
-    if (more) {
-      store_a(buf ^ 1, areg);
+  };
+
+  // Every step requests exactly one group (past the end: the last group
+  // again, into a ring slot nothing reads), so the requests stay in a fixed
+  // order the compiler's wait counts can follow. Ring slot and LDS stage of
+  // group g are both g % kMfD: group g + 1's activations are written while
+  // group g's are read, into the stage group g + 1 - kMfD left.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bq[j][0] = bq_next[j][0];
-        bq[j][1] = bq_next[j][1];
-        bs[j] = bs_next[j];
-      }
+  for (int d = 0; d < kMfD - 1; ++d) issue(min(d, G - 1), ring[d]);
+  stage_a(ring[0], 0);
+  for (int g0 = 0; g0 < G; g0 += kMfD) {
+#pragma unroll
+    for (int d = 0; d < kMfD; ++d) {
+      const int g = g0 + d;
+      __syncthreads();  // group g's stage is written; group g + 1's is free
+      issue(min(g + kMfD - 1, G - 1), ring[(d + kMfD - 1) % kMfD]);
+      if (g < G) compute(ring[d], d);
+      if (g + 1 < G) stage_a(ring[(d + 1) % kMfD], (d + 1) % kMfD);
     }
-    __syncthreads();
   }
 
   // epilogue: C layout of 32x32 MFMA: lane holds column l32, rows
