@@ -43,6 +43,9 @@ def parse():
                     help="layer: moe_layer_w4a16 (one call per layer; W4A16 only); "
                          "calls: the four separate calls. Default: layer for W4A16")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--units", type=int, default=None,
+                    help="stage only the first N units (short counter passes; per-launch "
+                         "figures do not depend on the number of units)")
     return ap.parse_args()
 
 
@@ -93,6 +96,8 @@ def main():
     torch.cuda.set_device(0)
     moe.load()
     wl = synth.workload(args.workload)
+    if args.units:
+        wl = wl.with_(units=min(args.units, wl.units))
     units = stage(wl, torch)
     bufs = [moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt) for _ in range(wl.units)]
     shape = (wl.T, wl.H, wl.I, wl.E, wl.k)
@@ -204,13 +209,17 @@ def main():
     avg_bytes = sum(act_per_unit[u] * eb + io_bytes for u in calls) / len(calls)
     achieved = avg_bytes / (avg_ms / 1e3) / 1e9
     flops_per_call = 6.0 * wl.H * wl.I * wl.T * wl.k
+    # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+    # a copy of known size), valid only for the kernel sources they were taken on
+    from quantized_moe_expert_top_amd import traffic as traffic_store
+    tr = traffic_store.lookup(wl.name)
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": tr["bytes_per_launch"] if tr else None,
         "kernel": kernel,
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "algo_bytes_per_launch": int(avg_bytes),

@@ -1,8 +1,9 @@
 // Streaming-read ceiling probe for one MI355X: back-to-back launches of a
 // plain 16-byte-load read kernel over slabs rotated through a 1 GiB buffer
 // (so consecutive launches do not reuse the MALL), timed with HIP events;
-// plus the back-to-back cost of an empty kernel. Also serves as the "known
-// size" read kernel when calibrating FETCH_SIZE counters.
+// plus the back-to-back cost of an empty kernel. With the argument "copy" it
+// runs a plain copy of known size instead, the reference dispatch for
+// calibrating the FETCH_SIZE and WRITE_SIZE counters.
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <vector>
@@ -20,7 +21,32 @@ __global__ __launch_bounds__(256) void rd(const uint4* __restrict__ p, size_t sl
   if (acc == 0x12345678u) out[blockIdx.x] = acc;
 }
 __global__ void empty_k(unsigned* out) { if (threadIdx.x == 12345) out[0] = 1; }
-int main() {
+// plain copy: each thread moves 8 x 16 B (one known-size read and write stream)
+__global__ __launch_bounds__(256) void cp(const uint4* __restrict__ src, uint4* __restrict__ dst) {
+  const size_t base = static_cast<size_t>(blockIdx.x) * 2048 + threadIdx.x;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = src[base + i * 256];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[base + i * 256] = v[i];
+}
+// "copy" mode: three launches of cp over 256 MiB (src) -> 256 MiB (dst); the
+// counter calibration divides what FETCH_SIZE / WRITE_SIZE report for these
+// dispatches by the 262144 KiB each of them moves.
+int copy_mode() {
+  const size_t bytes = size_t(256) << 20;
+  uint4 *src, *dst;
+  CK(hipMalloc(&src, bytes)); CK(hipMalloc(&dst, bytes));
+  CK(hipMemset(src, 1, bytes)); CK(hipMemset(dst, 0, bytes));
+  CK(hipDeviceSynchronize());
+  const int blocks = static_cast<int>(bytes / (2048 * 16));
+  for (int i = 0; i < 3; ++i) cp<<<blocks, 256>>>(src, dst);
+  CK(hipDeviceSynchronize());
+  printf("copy: 3 dispatches, each reads and writes %zu KiB\n", bytes >> 10);
+  return 0;
+}
+int main(int argc, char** argv) {
+  if (argc > 1 && argv[1][0] == 'c') return copy_mode();
   size_t maxbytes = size_t(1) << 30;
   uint4* buf; unsigned* out;
   CK(hipMalloc(&buf, maxbytes)); CK(hipMalloc(&out, 1 << 20));

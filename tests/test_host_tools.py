@@ -1,0 +1,66 @@
+"""Host-side tools (no GPU): the traffic summarizer and bench.py's contract
+on a multi-GPU request."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from quantized_moe_expert_top_amd import traffic  # noqa: E402
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, counter, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_kernel_means_and_copy_factor(tmp_path):
+    p = tmp_path / "c.csv"
+    _csv(p, [("cp(HIP_vector_type<unsigned int, 4u> const*, HIP_vector_type<unsigned int, 4u>*)",
+              "FETCH_SIZE", 131072.0)] * 3 + [("__amd_rocclr_fillBufferAligned", "FETCH_SIZE", 9.0)])
+    m = traffic.kernel_means(str(p))
+    assert m["__amd_rocclr_fillBufferAligned"] == (1, 9.0)
+    assert traffic.copy_factor(str(p)) == pytest.approx(0.5)
+
+
+def test_unit_sum_matches_patterns(tmp_path):
+    p = tmp_path / "f.csv"
+    _csv(p, [("void moe::(anonymous namespace)::decode_gateup_slot_kernel<16, 4, 2>(float const*)",
+              "FETCH_SIZE", 100.0),
+             ("void moe::(anonymous namespace)::decode_gateup_slot_kernel<16, 4, 2>(float const*)",
+              "FETCH_SIZE", 300.0),
+             ("void moe::(anonymous namespace)::decode_down_kernel<8, 3, 2>(unsigned short const*)",
+              "FETCH_SIZE", 50.0),
+             ("at::native::vectorized_elementwise_kernel<4>", "FETCH_SIZE", 1e6)])
+    kib, names = traffic.unit_kib(str(p), traffic.UNIT_KERNELS["decode_t2"][1])
+    assert kib == pytest.approx(250.0)          # mean of each kernel, summed
+    assert names == ["decode_down_kernel<8, 3, 2>", "decode_gateup_slot_kernel<16, 4, 2>"]
+
+
+def test_lookup_rejects_stale_sources(tmp_path, monkeypatch):
+    store = tmp_path / "traffic.json"
+    monkeypatch.setattr(traffic, "STORE", str(store))
+    entry = {"bytes_per_launch": 123, "source_sha256": traffic.source_hash()}
+    store.write_text(json.dumps({"decode_t2": entry}))
+    assert traffic.lookup("decode_t2")["bytes_per_launch"] == 123
+    store.write_text(json.dumps({"decode_t2": dict(entry, source_sha256="0" * 64)}))
+    assert traffic.lookup("decode_t2") is None
+    assert traffic.lookup("prefill_t512") is None
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
