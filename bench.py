@@ -185,6 +185,38 @@ def main():
     ms_per_step = ms_total / args.steps
     value = wl.T * args.steps / (ms_total / 1e3)   # each step carries T tokens
 
+    # spread: three more passes of K steps each, after the timed region
+    pass_ms = []
+    for _ in range(3):
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for i in range(args.steps):
+            run_step(i)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        pass_ms.append(a0.elapsed_time(a1) / args.steps)
+    spread = {"passes_ms_per_step": [round(x, 4) for x in pass_ms],
+              "median_ms_per_step": round(float(np.median(pass_ms)), 4)}
+
+    # cold-cache steps (large-expert decode): a 1 GiB write between steps,
+    # outside the timed window, evicts the 256 MB MALL before each step
+    if wl.name == "decode_large" and not args.eager:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = []
+        for i in range(len(schedule)):
+            scratch.zero_()
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            run_step(i)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del scratch
+        spread["cold_median_ms_per_step"] = round(float(np.median(cold)), 4)
+        spread["warm_ms_per_step"] = round(ms_per_step, 4)
+
     calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
     eb = expert_bytes(wl)
     if path == "layer":
@@ -192,7 +224,9 @@ def main():
         # layer's bytes); per-call time from the timed region itself
         avg_ms = ms_total / len(calls)
         io_bytes = wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 4  # x, logits, out
-        kernel = "moe_layer_w4a16 (whole layer: decode_gateup_kernel + decode_down_kernel at T <= 4)"
+        kernel = ("moe_layer_w4a16 (whole layer: fused decode gate/up + down kernels)"
+                  if wl.T <= 4 else
+                  "moe_layer_w4a16 (whole layer: route, permute, grouped MFMA FFN, combine)")
     else:
         # dominant kernel: the grouped FFN calls of the same K steps, back to
         # back on the same stream, timed with HIP events
@@ -250,6 +284,7 @@ def main():
                    "mean_active_experts": round(float(np.mean(list(act_per_unit.values()))), 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "spread": spread,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
@@ -258,11 +293,24 @@ def main():
 def cpu_baseline(wl, schedule, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
+    blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info) or blas
     except Exception:
         threads = 1
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 0
     done = 0
     el = 0.0
     arrs = None
@@ -290,7 +338,8 @@ def cpu_baseline(wl, schedule, budget_s):
         "kind": "oracle",
         "sample": (f"{done} of {wl.units} units of workload {wl.name} through the float64 numpy "
                    f"oracle (input generation excluded); "
-                   f"{per_unit:.3f} s per unit, scaled to {len(schedule[0])} units per step"),
+                   f"{per_unit:.3f} s per unit, scaled to {len(schedule[0])} units per step; "
+                   f"{cpu_model}, {affinity} cores in the affinity mask, {blas}"),
     }
 
 

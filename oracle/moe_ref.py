@@ -37,6 +37,10 @@ where each function states it:
      row), codes rint_half_even(x/s) clamped to [-127, 127]; the same rule for
      the activations x (one row per token) and for h (one row per routed slot);
      int8 x int8 -> exact integer accumulators; y = acc * s_row * s_channel.
+  R8 router projection ahead of the top-k: logits[t, e] = sum_h x[t, h] *
+     w_r[e, h] over the bf16 token rows and the bf16 router rows [E][H] (the
+     pages route on such logits; the workload hands them in, and the step that
+     makes them is the dense product of the two).
 """
 from __future__ import annotations
 
@@ -91,6 +95,11 @@ def route_topk(logits: np.ndarray, k: int):
     z = np.exp(sel - sel[:, :1])
     w = z / z.sum(axis=1, keepdims=True)
     return ids, w
+
+
+def router_projection(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """R8: router logits [T][E] = x . w_r^T on the bf16 values, in float64."""
+    return bf16_to_f64(x_bits) @ bf16_to_f64(wr_bits).T
 
 
 # ------------------------------------------------------------- permutation --

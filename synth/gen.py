@@ -14,6 +14,9 @@ Formats produced (the layer's storage formats, not its arithmetic):
     (output row, 128-wide K group), value fp16(0.02*|N(0,1)|) with subnormals kept.
   * W8A8 weights: int8 uniform on [-127, 127] with one float32 scale per output
     row, 0.01*|N(0,1)|.
+  * router projection weights (for the projection ahead of the top-k): bf16
+    bit patterns [E][H] of N(0, 1/H) draws, so x . w_e is about N(0, 1) like
+    the given logits.
 """
 from __future__ import annotations
 
@@ -23,7 +26,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-TAG_X, TAG_LOGITS, TAG_BIAS, TAG_W13, TAG_S13, TAG_W2, TAG_S2 = range(7)
+TAG_X, TAG_LOGITS, TAG_BIAS, TAG_W13, TAG_S13, TAG_W2, TAG_S2, TAG_WR = range(8)
 GROUP = 128
 
 
@@ -105,6 +108,12 @@ def expert_bias(wl: Workload, unit: int) -> np.ndarray:
 def router_logits(wl: Workload, unit: int) -> np.ndarray:
     z = rng_for(wl, unit, TAG_LOGITS).standard_normal((wl.T, wl.E))
     return (z + expert_bias(wl, unit)[None, :]).astype(np.float32)
+
+
+def router_weights(wl: Workload, unit: int) -> np.ndarray:
+    """bf16 bits [E][H] of the router projection, N(0, 1/H)."""
+    z = rng_for(wl, _wunit(wl, unit), TAG_WR).standard_normal((wl.E, wl.H), dtype=np.float32)
+    return bf16_bits_from_f32(z / np.float32(np.sqrt(wl.H)))
 
 
 def _wunit(wl: Workload, unit: int) -> int:

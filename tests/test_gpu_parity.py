@@ -379,3 +379,29 @@ def test_layer_entry_in_graph_replays():
         torch.cuda.synchronize()
         for i, b in enumerate(bufs):
             np.testing.assert_array_equal(to_np(b.out).view(np.uint32), eager[i])
+
+
+# ------------------------------------------------------- batch invariance --
+INVARIANCE_CASES = [
+    # T, tokens per sub-batch, path (layer entry: fused decode; calls: MFMA GEMM)
+    (4, 1, "layer"),   # persistent gate/up for the batch, slot-per-block alone
+    (4, 2, "layer"),
+    (40, 20, "calls"),
+]
+
+
+@pytest.mark.parametrize("case", INVARIANCE_CASES, ids=[f"t{c[0]}_{c[1]}_{c[2]}" for c in INVARIANCE_CASES])
+def test_batch_invariance(case):
+    """A token's layer output is bitwise the same whether it runs in a batch of
+    T or in a smaller batch: per output element the kernels take the same
+    arithmetic in the same order whatever else is in the batch."""
+    T, sub, path = case
+    wl = synth.Workload(f"inv_t{T}", 140 + T, T, 2048, 768, 128, 8, "w4a16", "normal", 1)
+    x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+    wts = stage_weights(wl, 0)
+    run = _layer_entry if path == "layer" else run_layer
+    _say("batch invariance", wl.name, T, sub, path)
+    full = run(wl, x, L, wts)
+    for t0 in range(0, T, sub):
+        part = run(wl.with_(T=sub), x[t0:t0 + sub], L[t0:t0 + sub], wts)
+        np.testing.assert_array_equal(part["out_bits"], full["out_bits"][t0:t0 + sub])

@@ -448,3 +448,56 @@ def test_planted_swapped_gate_up_is_caught():
     G, U = x @ W13[I:].T, x @ W13[:I].T          # planted: halves swapped
     bad = (oracle.silu(G) * U) @ W2.T
     assert not np.allclose(bad, d["out_value"], rtol=1e-6)
+
+
+# ------------------------------------------------------ router projection --
+def _bits(a):
+    return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+def test_router_projection_one_hot_rows_pick_router_columns():
+    """x = e_h (an exact bf16 one) selects column h of the router rows exactly."""
+    rng = np.random.default_rng(7)
+    E, H = 5, 16
+    wr = _bits(rng.standard_normal((E, H)))
+    x = np.zeros((H, H), np.float32)
+    x[np.arange(H), np.arange(H)] = 1.0
+    got = oracle.router_projection(_bits(x), wr)
+    np.testing.assert_array_equal(got, oracle.bf16_to_f64(wr).T)
+
+
+def test_router_projection_closed_forms():
+    # all ones: every logit is H; a row of twos against a row of 0.5: H
+    H = 256
+    ones = _bits(np.ones((2, H)))
+    np.testing.assert_array_equal(oracle.router_projection(ones, _bits(np.ones((3, H)))),
+                                  np.full((2, 3), float(H)))
+    np.testing.assert_array_equal(
+        oracle.router_projection(_bits(np.full((1, H), 2.0)), _bits(np.full((1, H), 0.5))),
+        [[float(H)]])
+
+
+def test_router_projection_against_fsum_loop():
+    """Brute force: a Python loop with exactly rounded sums on tiny shapes."""
+    rng = np.random.default_rng(11)
+    T, H, E = 3, 24, 5
+    xb, wb = _bits(rng.standard_normal((T, H))), _bits(rng.standard_normal((E, H)))
+    xv, wv = oracle.bf16_to_f64(xb), oracle.bf16_to_f64(wb)
+    want = np.array([[math.fsum(xv[t, h] * wv[e, h] for h in range(H)) for e in range(E)]
+                     for t in range(T)])
+    np.testing.assert_allclose(oracle.router_projection(xb, wb), want, rtol=0, atol=1e-12)
+
+
+def test_planted_transposed_router_is_caught():
+    """A copy that multiplies by the router rows untransposed (w_r treated as
+    [H][E]) fails the one-hot pin on a square shape."""
+    rng = np.random.default_rng(3)
+    H = 8
+    wr = _bits(rng.standard_normal((H, H)))
+    x = np.eye(H, dtype=np.float32)
+
+    def bad(x_bits, wr_bits):
+        return oracle.bf16_to_f64(x_bits) @ oracle.bf16_to_f64(wr_bits)
+
+    assert not np.array_equal(bad(_bits(x), wr), oracle.bf16_to_f64(wr).T)
+    np.testing.assert_array_equal(oracle.router_projection(_bits(x), wr), oracle.bf16_to_f64(wr).T)
