@@ -78,6 +78,19 @@ MOE_API const char* moe_last_error(void);
 MOE_API int moe_abi_version(void);
 
 /*
+ * moe_router_logits — router projection ahead of the top-k. [PV-verify]
+ * (router ids exact: they are decided on these logits)
+ * logits[t, e] = sum_h x[t, h] * w_router[e, h]: bf16 x bf16 products, exact
+ * in float32, accumulated in float32 in a fixed order (deterministic).
+ *   x        bf16    [T, H]  (input)
+ *   w_router bf16    [E, H]  (input; row e is expert e's router row)
+ *   logits   float32 [T, E]  (output; feeds moe_route_topk or moe_layer_w4a16)
+ * Requires H % 64 == 0, 1 <= E <= MOE_MAX_EXPERTS, T >= 0.
+ */
+MOE_API int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T,
+                      int32_t H, int32_t E, float* logits, void* stream);
+
+/*
  * moe_route_topk — top-k routing. [PV-verify] (router ids exact)
  * For each token t: topk_ids[t, 0..k) = the k largest logits[t, :] in
  * descending order, ties broken by the lower expert index (+0.0 and -0.0 are

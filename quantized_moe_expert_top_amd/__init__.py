@@ -11,10 +11,12 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import (  # noqa: F401
     MoeError, combine, grouped_w4a16_ffn, grouped_w8a8_ffn, layer_w4a16, layer_w4a16_workspace,
-    load, permute, permute_workspace, route_topk, w4a16_workspace, w8a8_workspace,
+    load, permute, permute_workspace, route_topk, router_logits, w4a16_workspace,
+    w8a8_workspace,
 )
 
-__all__ = ["MoeError", "LayerBuffers", "moe_forward", "moe_layer", "load", "route_topk",
+__all__ = ["MoeError", "LayerBuffers", "moe_forward", "moe_layer", "load", "router_logits",
+           "route_topk",
            "permute", "grouped_w4a16_ffn", "grouped_w8a8_ffn", "combine", "layer_w4a16"]
 
 

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN",
           4: "MOE_EWORKSPACE", 5: "MOE_EUNSUPPORTED", 6: "MOE_EDEVICE"}
 
-EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_route_topk",
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_router_logits",
+           "moe_route_topk",
            "moe_permute_workspace", "moe_permute", "moe_w4a16_workspace",
            "moe_grouped_w4a16_ffn", "moe_w8a8_workspace", "moe_grouped_w8a8_ffn",
            "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16")
@@ -63,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),
+        "moe_router_logits": (ctypes.c_int, [P, P, I32, I32, I32, P, P]),
         "moe_route_topk": (ctypes.c_int, [P, I32, I32, I32, P, P, P]),
         "moe_permute_workspace": (SZ, [I32, I32, I32]),
         "moe_permute": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
@@ -121,6 +123,16 @@ def _stream(stream) -> int | None:
 
 
 # ------------------------------------------------------------- raw calls ----
+def router_logits(x, w_router, logits, stream=None) -> None:
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, T * H * 2, "x")
+    _need(w_router, E * H * 2, "w_router")
+    _need(logits, T * E * 4, "logits")
+    _check("moe_router_logits", load().moe_router_logits(_ptr(x), _ptr(w_router), T, H, E,
+                                                         _ptr(logits), _stream(stream)))
+
+
 def route_topk(logits, k: int, topk_ids, topk_w, stream=None) -> None:
     T, E = logits.shape
     _need(logits, T * E * 4, "logits")

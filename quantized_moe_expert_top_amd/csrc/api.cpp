@@ -109,6 +109,24 @@ const char* moe_last_error(void) { return g_last_error; }
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
+                      int32_t E, float* logits, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  if (H < 64 || H % 64) return fail(MOE_ESHAPE, "H = %d must be a positive multiple of 64", H);
+  if (static_cast<long long>(T) * H >= (1LL << 31) || static_cast<long long>(E) * H >= (1LL << 31))
+    return fail(MOE_ESHAPE, "T*H or E*H does not fit int32");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(logits);
+  int st;
+  if ((st = check_device())) return st;
+  return launched(moe::launch_router_logits(x, w_router, T, H, E, logits,
+                                            static_cast<hipStream_t>(stream)),
+                  "moe_router_logits launch");
+}
+
 int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
                    float* topk_w, void* stream) {
   int st = check_route_dims(T, E, k);

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
+                                float* logits, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,
                              hipStream_t s);
 

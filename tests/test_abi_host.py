@@ -32,7 +32,7 @@ def header_functions():
 @needs_lib
 def test_exports_match_header():
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(LIB, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -180,3 +180,22 @@ def test_layer_w4a16_validation():
     dummy = torch.empty(64, dtype=torch.uint8)
     with pytest.raises(_lib.MoeError):
         _lib.layer_w4a16((4, 200, 128, 8, 2), *([dummy] * 15), dummy, stream=0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    ((A, B, -1, 256, 8, A), 1),          # T < 0
+    ((A, B, 2, 96, 8, A), 2),            # H not a multiple of 64
+    ((A, B, 2, 0, 8, A), 2),             # H = 0
+    ((A, B, 2, 256, 0, A), 2),           # E = 0
+    ((A, B, 2, 256, 1025, A), 2),        # E > MOE_MAX_EXPERTS
+    ((None, B, 2, 256, 8, A), 1),        # null x
+    ((A, None, 2, 256, 8, A), 1),        # null router rows
+    ((A, B, 2, 256, 8, None), 1),        # null logits
+    ((MIS, B, 2, 256, 8, A), 3),         # misaligned x
+    ((A, B, 0, 256, 8, None), 0),        # empty batch: nothing to check or launch
+])
+def test_router_logits_validation(args, status):
+    assert LIB.moe_router_logits(*args, None) == status
+    if status:
+        assert LIB.moe_last_error()

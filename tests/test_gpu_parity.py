@@ -405,3 +405,52 @@ def test_batch_invariance(case):
     for t0 in range(0, T, sub):
         part = run(wl.with_(T=sub), x[t0:t0 + sub], L[t0:t0 + sub], wts)
         np.testing.assert_array_equal(part["out_bits"], full["out_bits"][t0:t0 + sub])
+
+
+
+# ------------------------------------------------------ router projection --
+ROUTER_CASES = [
+    # name, wid, T, H, E
+    ("router_decode", 401, 2, 2048, 128),
+    ("router_ragged", 402, 45, 192, 40),      # partial token and expert tiles
+    ("router_prefill", 403, 512, 2048, 128),
+    ("router_large", 404, 2, 7168, 256),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES, ids=[c[0] for c in ROUTER_CASES])
+def test_router_logits_and_routing(case):
+    """Logits within the float32 summation bound of the float64 oracle; the ids
+    and weights routed from the GPU logits match the oracle's routing of those
+    same logits (both sides decide on identical float32 inputs)."""
+    import quantized_moe_expert_top_amd as moe
+    name, wid, T, H, E = case
+    wl = synth.Workload(name, wid, T, H, 128, E, 8, "w4a16", "none", 1)
+    x, wr = synth.x_bf16(wl, 0), synth.router_weights(wl, 0)
+    _say("router", name, T, H, E)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    moe.router_logits(to_dev(x), to_dev(wr), logits)
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+    moe.route_topk(logits, 8, ids, w)
+    torch.cuda.synchronize()
+    got = to_np(logits).astype(np.float64)
+    ref = oracle.router_projection(x, wr)
+    # float32 accumulation of H exact products: |err| <= H * 2^-24 * sum |x w|
+    mag = np.abs(oracle.bf16_to_f64(x)) @ np.abs(oracle.bf16_to_f64(wr)).T
+    assert np.all(np.abs(got - ref) <= H * 2.0 ** -24 * mag + 1e-30)
+    rid, rw = oracle.route_topk(to_np(logits), 8)
+    np.testing.assert_array_equal(to_np(ids), rid)
+    np.testing.assert_allclose(to_np(w), rw, rtol=0, atol=1e-6)
+
+
+def test_router_logits_deterministic():
+    import quantized_moe_expert_top_amd as moe
+    wl = synth.Workload("router_det", 405, 300, 1024, 128, 96, 8, "w4a16", "none", 1)
+    x, wr = to_dev(synth.x_bf16(wl, 0)), to_dev(synth.router_weights(wl, 0))
+    a = torch.empty((300, 96), dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    moe.router_logits(x, wr, a)
+    moe.router_logits(x, wr, b)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
