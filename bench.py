@@ -217,6 +217,41 @@ def main():
         spread["cold_median_ms_per_step"] = round(float(np.median(cold)), 4)
         spread["warm_ms_per_step"] = round(ms_per_step, 4)
 
+    # the router projection ahead of the top-k (logits = x . w_r^T) on this
+    # workload's shape, timed alone: a separate row, not part of the step
+    wr = torch.from_numpy(synth.router_weights(wl, 0).view(np.int16)).cuda()
+    x0 = units[0][0]
+    lg = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
+    n_router = 50
+    for _ in range(3):
+        moe.router_logits(x0, wr, lg)
+    torch.cuda.synchronize()
+    rg = None
+    if not args.eager:   # launches replayed from a graph: device time, not host launch rate
+        rg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rg):
+            for _ in range(n_router):
+                moe.router_logits(x0, wr, lg)
+        rg.replay()
+        torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    if rg is not None:
+        rg.replay()
+    else:
+        for _ in range(n_router):
+            moe.router_logits(x0, wr, lg)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    router_us = r0.elapsed_time(r1) * 1e3 / n_router
+    router_bytes = wl.T * wl.H * 2 + wl.E * wl.H * 2 + wl.T * wl.E * 4
+    router_row = {"kernel": "router_logits_kernel (moe_router_logits)",
+                  "avg_launch_us": round(router_us, 2),
+                  "algo_bytes_per_launch": router_bytes,
+                  "achieved_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
+                  "flops_per_launch": 2 * wl.T * wl.H * wl.E}
+
     calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
     eb = expert_bytes(wl)
     if path == "layer":
@@ -285,6 +320,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "spread": spread,
+        "router_projection": router_row,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

@@ -81,7 +81,8 @@ MOE_API int moe_abi_version(void);
  * moe_router_logits — router projection ahead of the top-k. [PV-verify]
  * (router ids exact: they are decided on these logits)
  * logits[t, e] = sum_h x[t, h] * w_router[e, h]: bf16 x bf16 products, exact
- * in float32, accumulated in float32 in a fixed order (deterministic).
+ * in float32, accumulated in float32 in a fixed order (deterministic; the
+ * order differs between T <= 8 and larger T).
  *   x        bf16    [T, H]  (input)
  *   w_router bf16    [E, H]  (input; row e is expert e's router row)
  *   logits   float32 [T, E]  (output; feeds moe_route_topk or moe_layer_w4a16)

@@ -1,6 +1,6 @@
 // Router projection ahead of the top-k: logits[t, e] = x[t, :] . w_r[e, :].
 //
-// One v_mfma_f32_32x32x16_bf16 tile per block: 32 tokens x 32 experts. The
+// Many tokens: one v_mfma_f32_32x32x16_bf16 tile per block: 32 tokens x 32 experts. The
 // four waves of a block split H into contiguous quarters; their partial tiles
 // are added in LDS in wave order, so the sum order is fixed (deterministic).
 // bf16 x bf16 products are exact in float32; accumulation is float32.
@@ -73,11 +73,62 @@ __global__ __launch_bounds__(kThreads) void router_logits_kernel(
   }
 }
 
+// Few tokens (T <= kGemvT): one wave per expert row, so E waves share the
+// router rows instead of E/32 tiles. Lane l takes the 16-byte chunks l,
+// l + 64, ... of the row and of each token row, accumulates v_dot2 products
+// per token, and the wave sum (fixed DPP order) gives the logit.
+constexpr int kGemvT = 8;
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) void router_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
+    float* __restrict__ logits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e_raw = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  const int e = min(e_raw, E - 1);   // past E: a valid row, not stored
+  const int C = H / 8;               // 16-byte chunks per row
+  const uint16_t* w = wr + static_cast<size_t>(e) * H;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+#pragma unroll 4
+  for (int c = lane; c < C; c += kWave) {
+    const uint4 wv = ld16(w + c * 8);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T) {
+        const uint4 xv = ld16(x + static_cast<size_t>(t) * H + c * 8);
+        acc[t] = dot2_bf16(wv.x, xv.x, acc[t]);
+        acc[t] = dot2_bf16(wv.y, xv.y, acc[t]);
+        acc[t] = dot2_bf16(wv.z, xv.z, acc[t]);
+        acc[t] = dot2_bf16(wv.w, xv.w, acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < T) {
+      const float v = wave_sum_f32(acc[t]);
+      if (lane == 0 && e_raw < E) logits[static_cast<size_t>(t) * E + e] = v;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                                 float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (T <= kGemvT) {
+    const int blocks = (E + kThreads / kWave - 1) / (kThreads / kWave);
+    if (T <= 2)
+      router_gemv_kernel<2><<<blocks, kThreads, 0, s>>>(x, wr, T, H, E, logits);
+    else if (T <= 4)
+      router_gemv_kernel<4><<<blocks, kThreads, 0, s>>>(x, wr, T, H, E, logits);
+    else
+      router_gemv_kernel<8><<<blocks, kThreads, 0, s>>>(x, wr, T, H, E, logits);
+    return hipGetLastError();
+  }
   const dim3 grid((T + 31) / 32, (E + 31) / 32), block(kThreads);
   router_logits_kernel<<<grid, block, 0, s>>>(x, wr, T, H, E, logits);
   return hipGetLastError();

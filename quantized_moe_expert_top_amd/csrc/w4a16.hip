@@ -68,38 +68,54 @@ struct GemvGeom {
 // plus each chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the
 // main loop (so all-8 codes cancel to an exact zero). Row m comes from
 // src + m * K.
-__device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int nrows, int K,
-                                           uint32_t* xs, float* bsum) {
+// Two (row, chunk) items per thread per pass, both loads issued before use.
+// Thread numbering starts at `first` (rotated), so a caller can keep the
+// staging off waves that are busy with something else.
+struct StageRegs {
+  uint4 v[2][4];
+};
+__device__ __forceinline__ void gemv_stage_load(const uint16_t* __restrict__ src, int nrows, int K,
+                                                int i0, StageRegs& r) {
   const int C = K / 32, n = nrows * C, nt = blockDim.x;
-  // two (row, chunk) items per thread per pass, both loads issued before use
-  for (int i0 = threadIdx.x; i0 < n; i0 += 2 * nt) {
-    uint4 xv[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = min(i0 + h * nt, n - 1);
-      const int m = i / C, c = i - m * C;
-      const uint16_t* p = src + static_cast<size_t>(m) * K + c * 32;
+  for (int h = 0; h < 2; ++h) {
+    const int i = min(i0 + h * nt, n - 1);
+    const int m = i / C, c = i - m * C;
+    const uint16_t* p = src + static_cast<size_t>(m) * K + c * 32;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) xv[h][v] = ld16(p + v * 8);
+    for (int v = 0; v < 4; ++v) r.v[h][v] = ld16(p + v * 8);
+  }
+}
+__device__ __forceinline__ void gemv_stage_store(int nrows, int K, int i0, const StageRegs& r,
+                                                 uint32_t* xs, float* bsum) {
+  const int C = K / 32, n = nrows * C, nt = blockDim.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = i0 + h * nt;
+    if (i >= n) break;
+    const int m = i / C, c = i - m * C;
+    float bias = 0.0f;
+    uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 q = pair_permute(r.v[h][v]);
+      bias = dot2_bf16(kBiasPair, q.x, bias);
+      bias = dot2_bf16(kBiasPair, q.y, bias);
+      bias = dot2_bf16(kBiasPair, q.z, bias);
+      bias = dot2_bf16(kBiasPair, q.w, bias);
+      dst[v] = q;
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = i0 + h * nt;
-      if (i >= n) break;
-      const int m = i / C, c = i - m * C;
-      float bias = 0.0f;
-      uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 q = pair_permute(xv[h][v]);
-        bias = dot2_bf16(kBiasPair, q.x, bias);
-        bias = dot2_bf16(kBiasPair, q.y, bias);
-        bias = dot2_bf16(kBiasPair, q.z, bias);
-        bias = dot2_bf16(kBiasPair, q.w, bias);
-        dst[v] = q;
-      }
-      bsum[m * C + c] = bias;
-    }
+    bsum[m * C + c] = bias;
+  }
+}
+__device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int nrows, int K,
+                                           uint32_t* xs, float* bsum, int first = 0) {
+  const int n = nrows * (K / 32), nt = blockDim.x;
+  const int me = (threadIdx.x + nt - first % nt) % nt;
+  for (int i0 = me; i0 < n; i0 += 2 * nt) {
+    StageRegs r;
+    gemv_stage_load(src, nrows, K, i0, r);
+    gemv_stage_store(nrows, K, i0, r, xs, bsum);
   }
 }
 
@@ -468,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
                                  n_active_out, rec);
     return;
   }
-  gemv_stage(x, T, H, xs, bsum);
+  gemv_stage(x, T, H, xs, bsum, T * kWave);  // waves T.. (the top-k waves are busy)
   __syncthreads();
   const int a = blockIdx.x / tiles;
   const int tile = blockIdx.x - a * tiles;
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
                                  n_active_out, rec);
     return;
   }
-  gemv_stage(x, T, H, xs, bsum);
+  gemv_stage(x, T, H, xs, bsum, T * kWave);  // waves T.. (the top-k waves are busy)
   __syncthreads();
 
   // active experts in order of first pick; p0 = slots with a smaller id (the
@@ -683,6 +699,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   // read straight from the record (slot clamped below min(R, E), id clamped to
   // [0, E): every record slot holds a valid expert, the clamps only keep the
   // address in bounds), alongside the count of active experts.
+  // the first pass of h rows goes out first: it depends on nothing
+  const int n_stage = R * C;
+  StageRegs h0;
+  gemv_stage_load(h, R, I, tid, h0);
   const int act = R < E ? R : E;
   const int na = rec[0];
   auto first_codes = [&](int q, Item& w) {
@@ -697,7 +717,12 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     s_p0[i] = rec[2 + 3 * i];
     s_m[i] = rec[3 + 3 * i];
   }
-  gemv_stage(h, R, I, xs, bsum);
+  gemv_stage_store(R, I, tid, h0, xs, bsum);
+  for (int i0 = tid + 2 * kThreads; i0 < n_stage; i0 += 2 * kThreads) {
+    StageRegs r;
+    gemv_stage_load(h, R, I, i0, r);
+    gemv_stage_store(R, I, i0, r, xs, bsum);
+  }
   __syncthreads();
   const int nitems = na * upb;
   auto load_item = [&](int q, Item& w) {

@@ -412,6 +412,7 @@ def test_batch_invariance(case):
 ROUTER_CASES = [
     # name, wid, T, H, E
     ("router_decode", 401, 2, 2048, 128),
+    ("router_t5_ragged", 406, 5, 192, 37),    # the few-token path with E % 4 != 0
     ("router_ragged", 402, 45, 192, 40),      # partial token and expert tiles
     ("router_prefill", 403, 512, 2048, 128),
     ("router_large", 404, 2, 7168, 256),
