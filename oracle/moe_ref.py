@@ -37,6 +37,11 @@ where each function states it:
      row), codes rint_half_even(x/s) clamped to [-127, 127]; the same rule for
      the activations x (one row per token) and for h (one row per routed slot);
      int8 x int8 -> exact integer accumulators; y = acc * s_row * s_channel.
+  R9 W4A8: the int4 g128 weights of R4 against per-token int8 activations
+     (the R7 rule): per 128-wide K group an exact integer dot product of the
+     activation codes with (q - 8), times the group's fp16 scale, summed over
+     groups, times the row's activation scale; SwiGLU; h re-quantized per
+     routed row by R7; the down projection the same way.
   R8 router projection ahead of the top-k: logits[t, e] = sum_h x[t, h] *
      w_r[e, h] over the bf16 token rows and the bf16 router rows [E][H] (the
      pages route on such logits; the workload hands them in, and the step that
@@ -236,6 +241,53 @@ def ffn_w8a8(x_bits: np.ndarray, perm: dict, k: int, get_expert) -> dict:
     return out
 
 
+# -------------------------------------------------------------------- W4A8 --
+def group_int_dots(codes: np.ndarray, Q: np.ndarray) -> np.ndarray:
+    """[rows][N][G]: exact integer dot products of int8 activation codes
+    [rows][K] with int weights Q [N][K], one per 128-wide K group."""
+    G = Q.shape[1] // GROUP
+    out = np.zeros((codes.shape[0], Q.shape[0], G), np.int64)
+    for g in range(G):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        out[:, :, g] = int_matmul_exact(codes[:, sl], Q[:, sl])
+    return out
+
+
+def ffn_w4a8(x_bits: np.ndarray, perm: dict, k: int, get_expert) -> dict:
+    """Grouped W4A8 FFN (R9). Rows in grouped order.
+    ``get_expert(e) -> (w13 packed [2I,H/2], s13 fp16 bits [2I,H/128],
+    w2 packed [H,I/2], s2 fp16 bits [H,I/128])`` (the W4A16 storage)."""
+    X = bf16_to_f64(x_bits).astype(np.float32)
+    xq, xs = quant_rows_int8(X)
+    off = perm["expert_offsets"]
+    R = int(off[-1])
+    H = X.shape[1]
+    out = {"xq": xq, "xs": xs}
+    h = hq = hs = Y = None
+    for e in perm["active"]:
+        w13, s13, w2, s2 = get_expert(int(e))
+        Q13 = unpack_int4(w13).astype(np.int64) - ZERO_POINT
+        Q2 = unpack_int4(w2).astype(np.int64) - ZERO_POINT
+        I = Q13.shape[0] // 2
+        if h is None:
+            h = np.zeros((R, I))
+            hq = np.zeros((R, I), np.int8)
+            hs = np.zeros(R, np.float32)
+            Y = np.zeros((R, H))
+        a, b = off[e], off[e + 1]
+        tok = perm["sorted_slot"][a:b] // k
+        A13 = group_int_dots(xq[tok], Q13)                        # [rows, 2I, G]
+        GU = (A13 * fp16_to_f64(s13)[None, :, :]).sum(axis=2)
+        GU *= xs[tok].astype(np.float64)[:, None]
+        he = silu(GU[:, :I]) * GU[:, I:]
+        h[a:b] = he
+        hq[a:b], hs[a:b] = quant_rows_int8(he.astype(np.float32))
+        A2 = group_int_dots(hq[a:b], Q2)                          # [rows, H, I/128]
+        Y[a:b] = (A2 * fp16_to_f64(s2)[None, :, :]).sum(axis=2) * hs[a:b].astype(np.float64)[:, None]
+    out.update(h=h, hq=hq, hs=hs, y=Y)
+    return out
+
+
 # ------------------------------------------------------------ whole layer --
 def moe_layer_w4a16(x_bits, logits, k, get_expert) -> dict:
     ids, w = route_topk(logits, k)
@@ -251,6 +303,16 @@ def moe_layer_w8a8(x_bits, logits, k, get_expert) -> dict:
     E = np.asarray(logits).shape[1]
     perm = permute(ids, E)
     r = ffn_w8a8(x_bits, perm, k, get_expert)
+    out = combine(r["y"], perm["slot_pos"], w)
+    r.update(ids=ids, w=w, perm=perm, out=out)
+    return r
+
+
+def moe_layer_w4a8(x_bits, logits, k, get_expert) -> dict:
+    ids, w = route_topk(logits, k)
+    E = np.asarray(logits).shape[1]
+    perm = permute(ids, E)
+    r = ffn_w4a8(x_bits, perm, k, get_expert)
     out = combine(r["y"], perm["slot_pos"], w)
     r.update(ids=ids, w=w, perm=perm, out=out)
     return r

@@ -61,6 +61,7 @@ WORKLOADS = {
     "decode_t2":    Workload("decode_t2", 2, 2, 2048, 768, 128, 8, "w4a16", "normal", 48),
     "prefill_t512": Workload("prefill_t512", 3, 512, 2048, 768, 128, 8, "w4a16", "normal", 48),
     "w8a8_t4096":   Workload("w8a8_t4096", 4, 4096, 2048, 768, 128, 8, "w8a8", "none", 4),
+    "w4a8_t512":    Workload("w4a8_t512", 7, 512, 2048, 768, 128, 8, "w4a8", "normal", 48),
     "decode_large": Workload("decode_large", 5, 2, 7168, 2048, 256, 8, "w4a16", "zipf", 16,
                              shared_weights=True),
 }

@@ -61,7 +61,7 @@ def expert_getter_w8(wl, unit):
 
 
 def stage_weights(wl, unit, experts=None):
-    if wl.fmt == "w4a16":
+    if wl.fmt in ("w4a16", "w4a8"):
         arrs = synth.layer_w4(wl, unit, experts)
     else:
         arrs = synth.layer_w8(wl, unit)

@@ -501,3 +501,90 @@ def test_planted_transposed_router_is_caught():
 
     assert not np.array_equal(bad(_bits(x), wr), oracle.bf16_to_f64(wr).T)
     np.testing.assert_array_equal(oracle.router_projection(_bits(x), wr), oracle.bf16_to_f64(wr).T)
+
+
+# ------------------------------------------------------------------- W4A8 --
+def _w4a8_small(seed=0, T=10, H=256, I=128, E=6, k=2):
+    wl = synth.Workload("w4a8_small", 95 + seed, T, H, I, E, k, "w4a8", "none", 1)
+    x = synth.x_bf16(wl, 0)
+    L = synth.router_logits(wl, 0)
+    get = lambda e: synth.expert_w4(wl, 0, e, "w13") + synth.expert_w4(wl, 0, e, "w2")  # noqa: E731
+    return wl, x, L, get
+
+
+def _w4a8_slot_bruteforce(x_row, w13, s13, w2, s2, I):
+    """One routed slot with explicit per-group int64 dot products (R9)."""
+    xq, xs = oracle.quant_rows_int8(x_row[None].astype(np.float32))
+    q13 = oracle.unpack_int4(w13).astype(np.int64) - 8
+    sc13 = oracle.fp16_to_f64(s13)
+    H = q13.shape[1]
+    gu = np.zeros(2 * I)
+    for n in range(2 * I):
+        tot = 0.0
+        for g in range(H // 128):
+            d = int(np.dot(xq[0, g * 128:(g + 1) * 128].astype(np.int64), q13[n, g * 128:(g + 1) * 128]))
+            tot += sc13[n, g] * d
+        gu[n] = tot * float(xs[0])
+    h = gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]
+    hq, hs = oracle.quant_rows_int8(h[None].astype(np.float32))
+    q2 = oracle.unpack_int4(w2).astype(np.int64) - 8
+    sc2 = oracle.fp16_to_f64(s2)
+    y = np.zeros(q2.shape[0])
+    for n in range(q2.shape[0]):
+        tot = 0.0
+        for g in range(I // 128):
+            d = int(np.dot(hq[0, g * 128:(g + 1) * 128].astype(np.int64), q2[n, g * 128:(g + 1) * 128]))
+            tot += sc2[n, g] * d
+        y[n] = tot * float(hs[0])
+    return y
+
+
+def test_w4a8_bruteforce_per_token():
+    wl, x, L, get = _w4a8_small()
+    r = oracle.moe_layer_w4a8(x, L, wl.k, get)
+    X = oracle.bf16_to_f64(x)
+    out = np.zeros((wl.T, wl.H))
+    for t in range(wl.T):
+        for j in range(wl.k):
+            e = int(r["ids"][t, j])
+            y = _w4a8_slot_bruteforce(X[t], *get(e), wl.I)
+            np.testing.assert_allclose(r["y"][r["perm"]["slot_pos"][t * wl.k + j]], y,
+                                       rtol=1e-12, atol=1e-12)
+            out[t] += r["w"][t, j] * y
+    np.testing.assert_allclose(r["out"], out, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a8_close_to_w4a16():
+    """Same weights; only the activation quantization differs."""
+    wl, x, L, get = _w4a8_small(seed=1, T=16)
+    a = oracle.moe_layer_w4a8(x, L, wl.k, get)["out"]
+    b = oracle.moe_layer_w4a16(x, L, wl.k, get)["out"]
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 3e-2
+
+
+def test_w4a8_zero_down_codes_give_exact_zero():
+    wl, x, L, get = _w4a8_small(seed=2)
+
+    def zero_w2(e):
+        w13, s13, w2, s2 = get(e)
+        return w13, s13, np.full_like(w2, 0x88), s2
+
+    assert np.all(oracle.moe_layer_w4a8(x, L, wl.k, zero_w2)["out"] == 0.0)
+
+
+def test_planted_w4a8_zero_point_sign_is_caught():
+    """A copy that adds the zero point instead of subtracting it fails the
+    brute force."""
+    wl, x, L, get = _w4a8_small(seed=3, T=4)
+
+    def bad_get(e):
+        w13, s13, w2, s2 = get(e)
+        # codes q -> 16 - q (mod 16) flips q - 8 into 8 - q for every code but 8
+        flip = lambda p: (((16 - (p & 15)) & 15) | (((16 - (p >> 4)) & 15) << 4)).astype(np.uint8)  # noqa: E731
+        return flip(w13), s13, flip(w2), s2
+
+    r = oracle.moe_layer_w4a8(x, L, wl.k, bad_get)
+    X = oracle.bf16_to_f64(x)
+    e = int(r["ids"][0, 0])
+    y = _w4a8_slot_bruteforce(X[0], *get(e), wl.I)
+    assert not np.allclose(r["y"][r["perm"]["slot_pos"][0]], y, rtol=1e-6)
