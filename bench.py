@@ -62,7 +62,7 @@ def stage(wl, torch):
     for u in range(wl.units):
         wu = 0 if wl.shared_weights else u
         if wu not in wcache:
-            arrs = synth.layer_w4(wl, wu) if wl.fmt == "w4a16" else synth.layer_w8(wl, wu)
+            arrs = synth.layer_w8(wl, wu) if wl.fmt == "w8a8" else synth.layer_w4(wl, wu)
             wcache[wu] = tuple(dev(a) for a in arrs)
             del arrs
         units.append((dev(synth.x_bf16(wl, u)), dev(synth.router_logits(wl, u)), wcache[wu]))
@@ -71,7 +71,7 @@ def stage(wl, torch):
 
 
 def expert_bytes(wl) -> int:
-    if wl.fmt == "w4a16":
+    if wl.fmt in ("w4a16", "w4a8"):
         return (2 * wl.I * wl.H // 2 + 2 * wl.I * (wl.H // 128) * 2
                 + wl.H * wl.I // 2 + wl.H * (wl.I // 128) * 2)
     return 2 * wl.I * wl.H + 2 * wl.I * 4 + wl.H * wl.I + wl.H * 4
@@ -101,7 +101,8 @@ def main():
     units = stage(wl, torch)
     bufs = [moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt) for _ in range(wl.units)]
     shape = (wl.T, wl.H, wl.I, wl.E, wl.k)
-    ffn = moe.grouped_w4a16_ffn if wl.fmt == "w4a16" else moe.grouped_w8a8_ffn
+    ffn = {"w4a16": moe.grouped_w4a16_ffn, "w4a8": moe.grouped_w4a8_ffn,
+           "w8a8": moe.grouped_w8a8_ffn}[wl.fmt]
     schedule = layers_per_step(wl)
 
     def ffn_call(u):
@@ -293,8 +294,8 @@ def main():
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "algo_bytes_per_launch": int(avg_bytes),
     }
-    if wl.fmt == "w8a8" or wl.T >= 512:
-        dt = "int8" if wl.fmt == "w8a8" else "bf16"
+    if wl.fmt != "w4a16" or wl.T >= 512:
+        dt = "bf16" if wl.fmt == "w4a16" else "int8"
         roofline["mfma_frac"] = round(flops_per_call / (avg_ms / 1e3) / 1e12 / MFMA_PEAK[dt], 4)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, schedule, args.cpu_budget_s)
@@ -309,10 +310,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8" if wl.fmt == "w8a8" else "bf16",
+        "dtype": "bf16" if wl.fmt == "w4a16" else "int8",
         "data": "synthetic (seeded; random int4/int8 expert weights, N(0,1) activations)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
-                   "format": "W4A16 g128" if wl.fmt == "w4a16" else "W8A8",
+                   "format": {"w4a16": "W4A16 g128", "w4a8": "W4A8 (int4 g128 weights, int8 per-token activations)",
+                              "w8a8": "W8A8"}[wl.fmt],
                    "layers_per_step": len(schedule[0]),
                    "launch": "eager" if args.eager else "hip_graph_per_step",
                    "path": path,
@@ -354,11 +356,13 @@ def cpu_baseline(wl, schedule, budget_s):
         # inputs are generated before the clock starts; only the oracle is timed
         x, L = synth.x_bf16(wl, u), synth.router_logits(wl, u)
         if arrs is None or not wl.shared_weights:
-            arrs = synth.layer_w4(wl, u) if wl.fmt == "w4a16" else synth.layer_w8(wl, u)
+            arrs = synth.layer_w8(wl, u) if wl.fmt == "w8a8" else synth.layer_w4(wl, u)
         get = lambda e, a=arrs: tuple(t[e] for t in a)  # noqa: E731
         t0 = time.perf_counter()
         if wl.fmt == "w4a16":
             oracle.moe_layer_w4a16(x, L, wl.k, get)
+        elif wl.fmt == "w4a8":
+            oracle.moe_layer_w4a8(x, L, wl.k, get)
         else:
             oracle.moe_layer_w8a8(x, L, wl.k, get)
         el += time.perf_counter() - t0

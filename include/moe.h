@@ -228,6 +228,38 @@ MOE_API int moe_grouped_w8a8_ffn(const moe_shape* shape, const uint16_t* x,
                          float* y, const moe_w8a8_debug* dbg,
                          void* ws, size_t ws_bytes, void* stream);
 
+typedef struct {
+  int8_t* xq;     /* [T, H]   per-token int8 activations                 */
+  float* xs;      /* [T]      their scales                               */
+  int8_t* hq;     /* [R, I]   per-row int8 h, grouped order (R = T*k)     */
+  float* hs;      /* [R]      its scales                                 */
+} moe_w4a8_debug;
+
+/*
+ * moe_grouped_w4a8_ffn — grouped SwiGLU expert FFN, int4 g128 weights x int8
+ * activations on int8 MFMA. [MR] (W4A8 beside W4A16; one weight layout)
+ * Weights are the W4A16 storage (codes q, W = (q - 8) * s per 128-wide K
+ * group). Token rows are quantized as for W8A8 (absmax / 127, half-even,
+ * [-127, 127]). Per grouped position p (expert e, token t), output n:
+ *   gate = xs[t] * sum_g s13[e, n, g] * sum_{k in g} xq[t, k] * (q13[e, n, k] - 8)
+ *   (each group's sum an exact integer; the sum over groups in float32),
+ *   up likewise with row I + n; h = silu(gate) * up (float32), quantized per
+ *   row -> hq[p, :], hs[p]; y[p, m] = hs[p] * sum_g s2[e, m, g] * (exact
+ *   group sums of hq[p, k] * (q2[e, m, k] - 8)), float32.
+ *   x bf16 [T, H]; w13/s13/w2/s2 as moe_grouped_w4a16_ffn; y float32
+ *   [T*k, H] (grouped order).
+ * Requires H % 128 == 0, I % 128 == 0. `dbg` may be NULL. `ws` must hold
+ * moe_w4a8_workspace(shape) bytes.
+ */
+MOE_API size_t moe_w4a8_workspace(const moe_shape* shape);
+MOE_API int moe_grouped_w4a8_ffn(const moe_shape* shape, const uint16_t* x,
+                         const uint8_t* w13, const uint16_t* s13,
+                         const uint8_t* w2, const uint16_t* s2,
+                         const int32_t* expert_offsets, const int32_t* sorted_slot,
+                         const int32_t* active, const int32_t* n_active,
+                         float* y, const moe_w4a8_debug* dbg,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /*
  * moe_combine — weighted sum of each token's k expert outputs.
  * out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[slot_pos[t*k + j], :],

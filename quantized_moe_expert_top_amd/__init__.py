@@ -10,14 +10,15 @@ from dataclasses import dataclass
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    MoeError, combine, grouped_w4a16_ffn, grouped_w8a8_ffn, layer_w4a16, layer_w4a16_workspace,
-    load, permute, permute_workspace, route_topk, router_logits, w4a16_workspace,
-    w8a8_workspace,
+    MoeError, combine, grouped_w4a16_ffn, grouped_w4a8_ffn, grouped_w8a8_ffn, layer_w4a16,
+    layer_w4a16_workspace, load, permute, permute_workspace, route_topk, router_logits,
+    w4a16_workspace, w4a8_workspace, w8a8_workspace,
 )
 
 __all__ = ["MoeError", "LayerBuffers", "moe_forward", "moe_layer", "load", "router_logits",
            "route_topk",
-           "permute", "grouped_w4a16_ffn", "grouped_w8a8_ffn", "combine", "layer_w4a16"]
+           "permute", "grouped_w4a16_ffn", "grouped_w4a8_ffn", "grouped_w8a8_ffn", "combine",
+           "layer_w4a16"]
 
 
 @dataclass
@@ -48,7 +49,8 @@ class LayerBuffers:
         R = T * k
         i32 = dict(dtype=torch.int32, device=device)
         pws = _lib.permute_workspace(T, E, k)
-        fws = (_lib.w4a16_workspace if fmt == "w4a16" else _lib.w8a8_workspace)(T, H, I, E, k)
+        fws = {"w4a16": _lib.w4a16_workspace, "w4a8": _lib.w4a8_workspace,
+               "w8a8": _lib.w8a8_workspace}[fmt](T, H, I, E, k)
         lws = _lib.layer_w4a16_workspace(T, H, I, E, k) if fmt == "w4a16" else 0
         return cls(
             T, H, I, E, k, fmt,
@@ -78,6 +80,9 @@ def moe_forward(b: LayerBuffers, x, logits, weights, debug=None, stream=None):
     if b.fmt == "w4a16":
         _lib.grouped_w4a16_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
                                b.n_active, b.y, b.ffn_ws, stream)
+    elif b.fmt == "w4a8":
+        _lib.grouped_w4a8_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
+                              b.n_active, b.y, b.ffn_ws, debug, stream)
     else:
         _lib.grouped_w8a8_ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active,
                               b.n_active, b.y, b.ffn_ws, debug, stream)

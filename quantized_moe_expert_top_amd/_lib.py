@@ -19,7 +19,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN",
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_router_logits",
            "moe_route_topk",
            "moe_permute_workspace", "moe_permute", "moe_w4a16_workspace",
-           "moe_grouped_w4a16_ffn", "moe_w8a8_workspace", "moe_grouped_w8a8_ffn",
+           "moe_grouped_w4a16_ffn", "moe_w4a8_workspace", "moe_grouped_w4a8_ffn",
+           "moe_w8a8_workspace", "moe_grouped_w8a8_ffn",
            "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16")
 
 
@@ -37,6 +38,11 @@ class MoeShape(ctypes.Structure):
 class MoeW8A8Debug(ctypes.Structure):
     _fields_ = [("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p), ("acc13", ctypes.c_void_p),
                 ("hq", ctypes.c_void_p), ("hs", ctypes.c_void_p), ("acc2", ctypes.c_void_p)]
+
+
+class MoeW4A8Debug(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p), ("hq", ctypes.c_void_p),
+                ("hs", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_permute": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
         "moe_w4a16_workspace": (SZ, [ctypes.POINTER(MoeShape)]),
         "moe_grouped_w4a16_ffn": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 11 + [SZ, P]),
+        "moe_w4a8_workspace": (SZ, [ctypes.POINTER(MoeShape)]),
+        "moe_grouped_w4a8_ffn": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 10 +
+                                 [ctypes.POINTER(MoeW4A8Debug), P, SZ, P]),
         "moe_w8a8_workspace": (SZ, [ctypes.POINTER(MoeShape)]),
         "moe_grouped_w8a8_ffn": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 10 +
                                  [ctypes.POINTER(MoeW8A8Debug), P, SZ, P]),
@@ -193,6 +202,35 @@ def grouped_w4a16_ffn(shape, x, w13, s13, w2, s2, expert_offsets, sorted_slot, a
         ctypes.byref(s), _ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
         _ptr(expert_offsets), _ptr(sorted_slot), _ptr(active), _ptr(n_active), _ptr(y),
         _ptr(ws), nbytes, _stream(stream)))
+
+
+def w4a8_workspace(T: int, H: int, I: int, E: int, k: int) -> int:
+    s = MoeShape(T, H, I, E, k)
+    return int(load().moe_w4a8_workspace(ctypes.byref(s)))
+
+
+def grouped_w4a8_ffn(shape, x, w13, s13, w2, s2, expert_offsets, sorted_slot, active,
+                     n_active, y, ws, debug: dict | None = None, stream=None) -> None:
+    T, H, I, E, k = shape
+    R = T * k
+    if T > 0 and H % 128 == 0 and I % 128 == 0:
+        _check_ffn_sizes(shape, x, expert_offsets, sorted_slot, active, n_active, y)
+        _need(w13, E * 2 * I * H // 2, "w13")
+        _need(s13, E * 2 * I * (H // 128) * 2, "s13")
+        _need(w2, E * H * I // 2, "w2")
+        _need(s2, E * H * (I // 128) * 2, "s2")
+        if debug:
+            for n, nb in (("xq", T * H), ("xs", T * 4), ("hq", R * I), ("hs", R * 4)):
+                _need(debug.get(n), nb, "debug." + n)
+    s = MoeShape(*shape)
+    dbg = None
+    if debug:
+        dbg = ctypes.byref(MoeW4A8Debug(*[_ptr(debug.get(n)) for n in ("xq", "xs", "hq", "hs")]))
+    nbytes = ws.numel() * ws.element_size()
+    _check("moe_grouped_w4a8_ffn", load().moe_grouped_w4a8_ffn(
+        ctypes.byref(s), _ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+        _ptr(expert_offsets), _ptr(sorted_slot), _ptr(active), _ptr(n_active), _ptr(y),
+        dbg, _ptr(ws), nbytes, _stream(stream)))
 
 
 def w8a8_workspace(T: int, H: int, I: int, E: int, k: int) -> int:

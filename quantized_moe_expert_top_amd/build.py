@@ -16,8 +16,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["api.cpp", "router.hip", "route.hip", "permute.hip", "w4a16.hip", "w8a8.hip",
-           "combine.hip"]
+SOURCES = ["api.cpp", "router.hip", "route.hip", "permute.hip", "w4a16.hip", "w4a8.hip",
+           "w8a8.hip", "combine.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

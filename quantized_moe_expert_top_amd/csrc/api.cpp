@@ -245,6 +245,46 @@ int moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16_t* x,
                   "moe_layer_w4a16 launch");
 }
 
+size_t moe_w4a8_workspace(const moe_shape* s) {
+  if (check_shape(s, MOE_GROUP, MOE_GROUP)) return 0;
+  return moe::w4a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
+}
+
+int moe_grouped_w4a8_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
+                         const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
+                         const int32_t* expert_offsets, const int32_t* sorted_slot,
+                         const int32_t* active, const int32_t* n_active, float* y,
+                         const moe_w4a8_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  if (st) return st;
+  if (s->T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(s13);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(s2);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slot);
+  REQUIRE_PTR(active);
+  REQUIRE_PTR(n_active);
+  REQUIRE_PTR(y);
+  moe::W4A8Debug d = {nullptr, nullptr, nullptr, nullptr};
+  if (dbg) {
+    d = {dbg->xq, dbg->xs, dbg->hq, dbg->hs};
+    const void* ps[4] = {d.xq, d.xs, d.hq, d.hs};
+    for (const void* p : ps)
+      if (p && !aligned16(p)) return fail(MOE_EALIGN, "a debug pointer is not 16-byte aligned");
+  }
+  const size_t need = moe::w4a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "w4a8 workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE_PTR(ws);
+  if ((st = check_device())) return st;
+  return launched(moe::launch_w4a8_ffn(s->T, s->H, s->I, s->E, s->k, x, w13, s13, w2, s2,
+                                       expert_offsets, sorted_slot, y, d, ws,
+                                       static_cast<hipStream_t>(stream)),
+                  "moe_grouped_w4a8_ffn launch");
+}
+
 size_t moe_w8a8_workspace(const moe_shape* s) {
   if (check_shape(s, 64, 64)) return 0;
   return moe::w8a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);

@@ -48,6 +48,18 @@ hipError_t launch_w8a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                            const int* active, const int* n_active, float* y,
                            const W8A8Debug& dbg, void* ws, hipStream_t s);
 
+struct W4A8Debug {
+  int8_t* xq;
+  float* xs;
+  int8_t* hq;
+  float* hs;
+};
+size_t w4a8_workspace_bytes(int T, int H, int I, int E, int k);
+hipError_t launch_w4a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
+                           const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
+                           const uint16_t* s2, const int* offsets, const int* sorted_slot,
+                           float* y, const W4A8Debug& dbg, void* ws, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int* slot_pos, const float* w, int T, int H,
                           int k, float* out, hipStream_t s);
 

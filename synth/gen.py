@@ -39,7 +39,7 @@ class Workload:
     I: int            # expert intermediate size
     E: int            # experts
     k: int            # experts per token
-    fmt: str          # "w4a16" | "w8a8"
+    fmt: str          # "w4a16" | "w4a8" | "w8a8"
     bias: str         # "none" | "normal" | "zipf"
     units: int        # layers (or decode steps) in one timed pass
     shared_weights: bool = False   # all units use the weights of unit 0
@@ -52,10 +52,12 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five layer workloads: a tiny correctness case, decode of two concurrent
+# The layer workloads: a tiny correctness case, decode of two concurrent
 # requests over 48 independent layers, a 512-token prefill over 48 layers, a
 # 4096-token W8A8 prefill (rotated over 4 seeded layers so one layer's weights
-# are never cache-warm) and a large-expert decode over 16 steps of one layer.
+# are never cache-warm), a large-expert decode over 16 steps of one layer, and
+# the 512-token prefill again in the W4A8 format (int4 weights, int8
+# activations).
 WORKLOADS = {
     "tiny":         Workload("tiny", 1, 16, 256, 128, 8, 2, "w4a16", "none", 1),
     "decode_t2":    Workload("decode_t2", 2, 2, 2048, 768, 128, 8, "w4a16", "normal", 48),

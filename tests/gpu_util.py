@@ -82,6 +82,14 @@ def run_layer(wl, x_bits, logits, weights, debug=False):
             "hs": torch.empty(R, dtype=torch.float32, device="cuda"),
             "acc2": torch.empty((R, wl.H), dtype=torch.int32, device="cuda"),
         }
+    if debug and wl.fmt == "w4a8":
+        R = wl.T * wl.k
+        dbg = {
+            "xq": torch.empty((wl.T, wl.H), dtype=torch.int8, device="cuda"),
+            "xs": torch.empty(wl.T, dtype=torch.float32, device="cuda"),
+            "hq": torch.empty((R, wl.I), dtype=torch.int8, device="cuda"),
+            "hs": torch.empty(R, dtype=torch.float32, device="cuda"),
+        }
     moe.moe_forward(b, to_dev(x_bits), to_dev(logits), weights, debug=dbg)
     torch.cuda.synchronize()
     R = wl.T * wl.k

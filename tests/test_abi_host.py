@@ -32,7 +32,7 @@ def header_functions():
 @needs_lib
 def test_exports_match_header():
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(LIB, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -120,6 +120,29 @@ def test_w4a16_validation():
 
 
 @needs_lib
+def test_w4a8_validation():
+    f = LIB.moe_grouped_w4a8_ffn
+    s = _shape()
+    need = _lib.w4a8_workspace(4, 256, 128, 8, 2)
+    # xq, xs, group sums of x; h float32; hq, hs, group sums of h (256-byte aligned each)
+    assert need == 1024 + 256 + 256 + 4096 + 1024 + 256 + 256
+    ok = [A] * 10
+    assert f(ctypes.byref(_shape(H=192)), *ok, None, A, need, None) == 2     # H % 128
+    assert f(ctypes.byref(_shape(I=64)), *ok, None, A, need, None) == 2      # I % 128
+    assert f(ctypes.byref(_shape(k=9)), *ok, None, A, need, None) == 2
+    assert f(None, *ok, None, A, need, None) == 1
+    assert f(ctypes.byref(s), *ok, None, A, need - 1, None) == 4
+    bad = list(ok)
+    bad[9] = None                                                        # y
+    assert f(ctypes.byref(s), *bad, None, A, need, None) == 1
+    dbg = _lib.MoeW4A8Debug(A, A, MIS, None)
+    assert f(ctypes.byref(s), *ok, ctypes.byref(dbg), A, need, None) == 3
+    assert f(ctypes.byref(_shape(T=0)), *([None] * 10), None, None, 0, None) == 0
+    assert _lib.w4a8_workspace(4, 192, 128, 8, 2) == 0
+    if _no_gpu():
+        assert f(ctypes.byref(s), *ok, None, A, need, None) == 6
+
+
 def test_w8a8_validation():
     f = LIB.moe_grouped_w8a8_ffn
     s = _shape(H=192, I=64)          # W8A8 needs multiples of 64 only
