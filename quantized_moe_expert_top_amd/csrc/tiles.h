@@ -7,7 +7,9 @@ namespace moe {
 // Locate this block's (expert, m-tile, n-tile). Tiles are ordered expert by
 // expert, n-tile major and m-tile minor, so m-tiles that share a weight strip
 // are adjacent; each XCD (blockIdx % 8) takes a contiguous run of tiles, so
-// those neighbours share that XCD's L2.
+// those neighbours share that XCD's L2. The expert's row range comes back
+// through LDS with the tile (one round trip to memory in all); `sm_out` holds
+// 5 ints.
 struct TileInfo {
   int e, mt, nt, p_begin, p_end;
 };
@@ -17,15 +19,18 @@ __device__ bool find_tile(const int* __restrict__ offsets, int E, int NT, int* s
                           int* sm_out, TileInfo& ti) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int ept = (E + NTHREADS - 1) / NTHREADS;  // <= 4
-  int cnt[4], sum = 0;
+  int cnt[4], beg[4], rows_of[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * ept + i;
-    int c = 0;
+    int c = 0, b = 0, rows = 0;
     if (i < ept && e < E) {
-      const int rows = offsets[e + 1] - offsets[e];
+      b = offsets[e];
+      rows = offsets[e + 1] - b;
       c = (rows + BM - 1) / BM * NT;
     }
+    beg[i] = b;
+    rows_of[i] = rows;
     cnt[i] = c;
     sum += c;
   }
@@ -57,6 +62,8 @@ __device__ bool find_tile(const int* __restrict__ offsets, int E, int NT, int* s
       sm_out[0] = e;
       sm_out[1] = local % mtiles;
       sm_out[2] = local / mtiles;
+      sm_out[3] = beg[i];
+      sm_out[4] = beg[i] + rows_of[i];
     }
     start += cnt[i];
   }
@@ -65,8 +72,8 @@ __device__ bool find_tile(const int* __restrict__ offsets, int E, int NT, int* s
   ti.e = sm_out[0];
   ti.mt = sm_out[1];
   ti.nt = sm_out[2];
-  ti.p_begin = offsets[ti.e] + ti.mt * BM;
-  ti.p_end = offsets[ti.e + 1];
+  ti.p_begin = sm_out[3] + ti.mt * BM;
+  ti.p_end = sm_out[4];
   return true;
 }
 

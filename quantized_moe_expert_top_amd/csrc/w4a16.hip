@@ -1015,7 +1015,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kMfD * STAGE];
   __shared__ int row_src[BM];
   __shared__ int sm_pref[kThreads / kWave];
-  __shared__ int sm_out[3];
+  __shared__ int sm_out[5];
 
   TileInfo ti;
   if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;

@@ -3,15 +3,18 @@
 //
 // "Measured results", section "Speed": W4A8 beside W4A16 as a weight path.
 //   1. quant: per row, s = absmax/127 (IEEE float32 division), codes
-//      rint(x/s) clamped to [-127, 127]; also the sum of each 128-wide group
-//      of codes (for the zero point).
+//      rint(x/s) clamped to [-127, 127]. The GEMM operand copy holds each
+//      8-code chunk in the order {0,2,4,6,1,3,5,7} (the order the weight
+//      unpacking below produces); the debug copy is in natural order.
 //   2. gate/up: v_mfma_i32_32x32x32_i8 over (expert, 32-row, 128 h-column)
-//      tiles. Codes 0..15 are unpacked to int8 as stored; per 128-k group the
-//      exact integer dot is corrected by 8 * (group code sum), scaled by the
-//      group's fp16 scale and accumulated in float32; the epilogue applies the
-//      row scale and SwiGLU, writing h float32 in grouped order.
+//      tiles. A code c becomes the int8 16*(c - 8): the nibble xor 8 (its
+//      two's complement 4-bit value) placed in the high half of a byte, so
+//      the integer dot of a 128-k group is exact and needs no zero-point
+//      correction; each group's dot is scaled by the group's fp16 scale and
+//      accumulated in float32; the epilogue applies row scale / 16 (exact)
+//      and SwiGLU, writing h float32 in grouped order.
 //   3. h quant: step 1 on h, one row per routed slot.
-//   4. down: step 2 on hq against W2; y = hs * acc, float32.
+//   4. down: step 2 on hq against W2; y = hs/16 * acc, float32.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -20,7 +23,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 32;     // rows per tile
 constexpr int kD = 3;       // 128-k groups in flight
 
 // --------------------------------------------------------- quantization ----
@@ -52,13 +54,11 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 }
 
 // One wave per row of K values (bf16 x rows or float32 h rows), K % 128 == 0.
-// Lane l takes 8-value chunks l, l + 64, ...; a 128-wide group is 16 chunks,
-// i.e. one 16-lane row of the wave, so its code sum is a row reduction.
+// Lane l takes 8-value chunks l, l + 64, ...
 template <typename T>
-__global__ __launch_bounds__(kThreads) void quant_gsum_kernel(const T* __restrict__ src, int rows,
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T* __restrict__ src, int rows,
                                                               int K, int8_t* __restrict__ q,
                                                               float* __restrict__ scale,
-                                                              int* __restrict__ gsum,
                                                               int8_t* __restrict__ dbg_q,
                                                               float* __restrict__ dbg_s) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -76,27 +76,19 @@ __global__ __launch_bounds__(kThreads) void quant_gsum_kernel(const T* __restric
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
   const float s = amax / 127.0f;
-  for (int c0 = 0; c0 < C; c0 += kWave) {   // uniform trip count: all lanes reduce
-    const int c = c0 + lane;
-    int sum = 0;
-    if (c < C) {
-      float v[8];
-      load8(row + c * 8, v);
-      uint32_t packed[2] = {0, 0};
+  for (int c = lane; c < C; c += kWave) {
+    float v[8];
+    load8(row + c * 8, v);
+    uint32_t nat[2] = {0, 0}, op[2] = {0, 0};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int code = quant_code4a8(v[i], s);
-        sum += code;
-        packed[i >> 2] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (i & 3));
-      }
-      const uint2 pv = make_uint2(packed[0], packed[1]);
-      *reinterpret_cast<uint2*>(q + static_cast<size_t>(r) * K + c * 8) = pv;
-      if (dbg_q) *reinterpret_cast<uint2*>(dbg_q + static_cast<size_t>(r) * K + c * 8) = pv;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = static_cast<uint32_t>(quant_code4a8(v[i], s)) & 0xFFu;
+      nat[i >> 2] |= b << (8 * (i & 3));
+      op[i & 1] |= b << (8 * (i >> 1));   // even k in dword 0, odd k in dword 1
     }
-    // sum over the 16 chunks of each group (16-lane rows of the wave)
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) sum += wave_shfl_xor(sum, m);
-    if ((lane & 15) == 0 && c < C) gsum[static_cast<size_t>(r) * (K / 128) + c / 16] = sum;
+    *reinterpret_cast<uint2*>(q + static_cast<size_t>(r) * K + c * 8) = make_uint2(op[0], op[1]);
+    if (dbg_q)
+      *reinterpret_cast<uint2*>(dbg_q + static_cast<size_t>(r) * K + c * 8) = make_uint2(nat[0], nat[1]);
   }
   if (lane == 0) {
     scale[r] = s;
@@ -110,45 +102,34 @@ __global__ __launch_bounds__(kThreads) void quant_gsum_kernel(const T* __restric
 // KIND 1: down. Wave w owns W2 rows [nt*256 + 64w, +64) as two subtiles.
 // K order inside a 128-k group: lane half hf takes k = 64*hf + [0, 64); MFMA
 // step s (of 4) takes k = 64*hf + 16*s + [0, 16) for that half, on both
-// operands (natural order: 16 consecutive codes / activation bytes).
+// operands, whose 16 bytes hold those k in the order {0,2,4,6,1,3,5,7,
+// 8,10,12,14,9,11,13,15} (the activation codes are stored that way; the
+// weight unpacking yields it).
 // Per group: codes of the group (32 bytes per lane and subtile) and the raw
 // fp16 scales stream through a register ring of kD groups, with this thread's
 // 16-byte share of the activation tile; the activation tile is written to a
 // swizzled LDS stage one step before use (two stages).
-template <int KIND>
+template <int KIND, int MT>
 __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
-    const int* __restrict__ a_gsum, const uint8_t* __restrict__ W,
-    const uint16_t* __restrict__ S, const int* __restrict__ offsets,
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S, const int* __restrict__ offsets,
     const int* __restrict__ sorted_slot, float* __restrict__ out, int K, int N, int E, int topk,
     int NT) {
-  constexpr int STAGE = kBM * 128;   // bytes of one activation stage
+  constexpr int BM = 32 * MT;        // tile rows: MT m-subtiles of 32 share each B fragment
+  constexpr int STAGE = BM * 128;    // bytes of one activation stage
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * STAGE];
-  __shared__ int row_src[kBM];
-  __shared__ float row_scale[kBM];
+  __shared__ int row_src[BM];
+  __shared__ float row_scale[BM];
   __shared__ int sm_pref[kThreads / kWave];
-  __shared__ int sm_out[3];
-  extern __shared__ int gs_lds[];   // [kBM][G]: 8 * group code sums of the tile rows
+  __shared__ int sm_out[5];
+  extern __shared__ uint16_t s_lds[];   // [256][G]: fp16 scales of the tile's weight rows
 
   TileInfo ti;
-  if (!find_tile<kBM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
+  if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int G = K / kGroup;
-
-  if (tid < kBM) {
-    const int p = ti.p_begin + tid;
-    const int pv = p < ti.p_end ? p : ti.p_begin;
-    const int src = (KIND == 0) ? sorted_slot[pv] / topk : pv;
-    row_src[tid] = src;
-    row_scale[tid] = a_scale[src];
-  }
-  __syncthreads();
-  for (int i = tid; i < kBM * G; i += kThreads) {
-    const int m = i / G, g = i - m * G;
-    gs_lds[i] = 8 * a_gsum[static_cast<size_t>(row_src[m]) * G + g];
-  }
 
   int nrow[2];
   bool nvalid[2];
@@ -171,29 +152,40 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * rowb, static_cast<uint32_t>(N) * rowb);
   const __amdgpu_buffer_rsrc_t s_rsrc =
       buffer_rsrc(S + static_cast<size_t>(ti.e) * N * G, static_cast<uint32_t>(N * G) * 2u);
-  uint32_t woff[2], soff[2];
+  uint32_t woff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
-    soff[j] = static_cast<uint32_t>(nrow[j] * G) * 2u;
-  }
-  // this thread's activation chunk: slot L = tid of a stage holds row L/8,
-  // 16-byte chunk (L%8) ^ ((row/2)%8)
-  const int arow = tid >> 3;
-  const int8_t* asrc = A + static_cast<size_t>(row_src[arow]) * K + ((tid & 7) ^ ((arow >> 1) & 7)) * 16;
-  const int adst = tid * 16;
-  // LDS offsets of this lane's A operand for the 4 MFMA steps of a group
-  int aoffs[4];
+  for (int j = 0; j < 2; ++j) woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
+  // this lane's rows within the tile's 256 scale rows
+  int srow[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) aoffs[s] = (l32 * 8 + ((hf * 4 + s) ^ ((l32 >> 1) & 7))) * 16;
+  for (int j = 0; j < 2; ++j) srow[j] = (KIND == 0) ? j * 128 + wv * 32 + l32 : wv * 64 + j * 32 + l32;
+
+  // The scales of the tile's 256 weight rows are contiguous runs of S (two
+  // 128-row strips, gate and up, or one 256-row strip) starting at multiples
+  // of 256 bytes: they are copied to LDS in 16-byte chunks (a per-group load
+  // of one fp16 per row would touch 32 rows per instruction). Rows past the
+  // expert read as 0 through the buffer resource and are never used. Loads
+  // and stores are unconditional (clamped) so all stay in flight together.
+  constexpr int kScBatch = 4;
+  const int sc_chunks = 32 * G;           // 256 rows * G * 2 bytes / 16
+  const uint32_t strip0 = static_cast<uint32_t>((KIND == 0 ? ti.nt * 128 : ti.nt * 256) * G * 2);
+  const uint32_t strip1 = static_cast<uint32_t>((N / 2 + ti.nt * 128) * G * 2);
+  uint4 scv[kScBatch];
+  auto sc_src = [&](int i) -> uint32_t {
+    if (KIND == 0 && i >= 16 * G) return strip1 + (i - 16 * G) * 16;
+    return strip0 + i * 16;
+  };
+#pragma unroll
+  for (int u = 0; u < kScBatch; ++u)
+    scv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           s_rsrc, sc_src(min(u * kThreads + tid, sc_chunks - 1)), 0, 0));
 
   struct Grp {
     uint4 q[2][2];
-    uint32_t sc[2];
-    uint4 a;
+    uint4 a[MT];
   };
   Grp ring[kD];
-  auto issue = [&](int g, Grp& b) {
+  auto issue_w = [&](int g, Grp& b) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       b.q[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -201,70 +193,135 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
       b.q[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 w_rsrc, woff[j] + 16, g * 64, 0));
     }
-    b.a = ld16(asrc + g * kGroup);
+  };
+  // the weight strip does not depend on the rows: start streaming it first
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, soff[j], g * 2, 0);
+  for (int d = 0; d < kD - 1; ++d) issue_w(min(d, G - 1), ring[d]);
+
+  int my_src = 0;
+  if (tid < BM) {
+    const int p = ti.p_begin + tid;
+    const int pv = p < ti.p_end ? p : ti.p_begin;
+    my_src = (KIND == 0) ? sorted_slot[pv] / topk : pv;
+    row_src[tid] = my_src;
+  }
+  __syncthreads();
+  // the row scale is needed only by the epilogue: its load overlaps the
+  // first activation loads
+  float my_scale = 0.0f;
+  if (tid < BM) my_scale = a_scale[my_src];
+  // this thread's activation chunks: slot L = tid + 256 i of a stage holds
+  // row L/8, 16-byte chunk (L%8) ^ ((row/2)%8); the xor term is the same for
+  // rows 32 apart
+  const int arow = tid >> 3, achunk = ((tid & 7) ^ ((arow >> 1) & 7)) * 16;
+  const int8_t* asrc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    asrc[i] = A + static_cast<size_t>(row_src[arow + 32 * i]) * K + achunk;
+  const int adst = tid * 16;
+#pragma unroll
+  for (int d = 0; d < kD - 1; ++d)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) ring[d].a[i] = ld16(asrc[i] + min(d, G - 1) * kGroup);
+
+  // LDS offsets of this lane's A operand for the 4 MFMA steps of a group
+  // (m-subtile i adds 32 rows = 4096 bytes)
+  int aoffs[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoffs[s] = (l32 * 8 + ((hf * 4 + s) ^ ((l32 >> 1) & 7))) * 16;
+
+  auto issue = [&](int g, Grp& b) {
+    issue_w(g, b);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) b.a[i] = ld16(asrc[i] + g * kGroup);
+  };
+  auto stage_a = [&](const Grp& b, int stage) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      *reinterpret_cast<uint4*>(a_lds + stage * STAGE + i * 4096 + adst) = b.a[i];
   };
 
-  float acc[2][16];
+  float acc[MT][2][16];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // 8 codes (one dword, byte b = k(2b) | k(2b+1) << 4) -> 8 int8 in k order
-  auto unpack = [](uint32_t w, uint32_t& d0, uint32_t& d1) {
-    const uint32_t t = w >> 4;
-    d0 = __builtin_amdgcn_perm(t, w, 0x05010400u) & 0x0F0F0F0Fu;
-    d1 = __builtin_amdgcn_perm(t, w, 0x07030602u) & 0x0F0F0F0Fu;
+  // 8 codes (one dword, byte b = k(2b) | k(2b+1) << 4) -> 8 int8 holding
+  // 16 * (code - 8): e = {k0, k2, k4, k6}, o = {k1, k3, k5, k7}
+  const uint32_t kFlip = 0x88888888u, kHiN = 0xF0F0F0F0u;
+  auto unpack = [&](uint32_t w, uint32_t& e, uint32_t& o) {
+    const uint32_t f = w ^ kFlip;
+    e = (f << 4) & kHiN;
+    o = f & kHiN;
   };
   auto compute = [&](const Grp& b, int stage, int g) {
     const uint8_t* st = a_lds + stage * STAGE;
-    uint4 av[4];
+    uint4 av[MT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const uint4*>(st + aoffs[s]);
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        av[i][s] = *reinterpret_cast<const uint4*>(st + i * 4096 + aoffs[s]);
+    uint16_t sc_bits[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sc_bits[j] = s_lds[srow[j] * G + g];
     __builtin_amdgcn_sched_barrier(0);
-    i32x16_t accg[2];
+    i32x16_t accg[MT][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accg[j][r] = 0;
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accg[i][j][r] = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const i32x4_t aop = __builtin_bit_cast(i32x4_t, av[s]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // step s uses bytes [8s, 8s + 8) of the lane's 32 code bytes
         const uint32_t w0 = (&b.q[j][s >> 1].x)[(s & 1) * 2];
         const uint32_t w1 = (&b.q[j][s >> 1].x)[(s & 1) * 2 + 1];
+        uint32_t e0, o0, e1, o1;
+        unpack(w0, e0, o0);
+        unpack(w1, e1, o1);
         i32x4_t bop;
-        uint32_t d0, d1, d2, d3;
-        unpack(w0, d0, d1);
-        unpack(w1, d2, d3);
-        bop[0] = static_cast<int>(d0);
-        bop[1] = static_cast<int>(d1);
-        bop[2] = static_cast<int>(d2);
-        bop[3] = static_cast<int>(d3);
-        accg[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop, accg[j], 0, 0, 0);
+        bop[0] = static_cast<int>(e0);
+        bop[1] = static_cast<int>(o0);
+        bop[2] = static_cast<int>(e1);
+        bop[3] = static_cast<int>(o1);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          accg[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              __builtin_bit_cast(i32x4_t, av[i][s]), bop, accg[i][j], 0, 0, 0);
       }
     }
-    // exact integer correction for the zero point, then the group scale
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const float sc = fp16_bits_to_f32(static_cast<uint16_t>(b.sc[j]));
+      const float sc = fp16_bits_to_f32(sc_bits[j]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = (r >> 2) * 8 + hf * 4 + (r & 3);
-        acc[j][r] += sc * static_cast<float>(accg[j][r] - gs_lds[m * G + g]);
-      }
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += sc * static_cast<float>(accg[i][j][r]);
     }
   };
 
-  asm volatile("" ::"s"(out));
+  // scale strips into LDS (read after the loop's first barrier)
+  for (int i0 = 0; i0 < sc_chunks; i0 += kScBatch * kThreads) {
+    if (i0 > 0) {
 #pragma unroll
-  for (int d = 0; d < kD - 1; ++d) issue(min(d, G - 1), ring[d]);
-  *reinterpret_cast<uint4*>(a_lds + adst) = ring[0].a;
+      for (int u = 0; u < kScBatch; ++u)
+        scv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               s_rsrc, sc_src(min(i0 + u * kThreads + tid, sc_chunks - 1)), 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kScBatch; ++u)
+      *reinterpret_cast<uint4*>(s_lds + min(i0 + u * kThreads + tid, sc_chunks - 1) * 8) = scv[u];
+  }
+  asm volatile("" ::"s"(out));
+  stage_a(ring[0], 0);
+  if (tid < BM) row_scale[tid] = my_scale;   // read after the loop's barriers
   for (int g0 = 0; g0 < G; g0 += kD) {
 #pragma unroll
     for (int d = 0; d < kD; ++d) {
@@ -272,56 +329,62 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
       __syncthreads();  // group g's stage is written; group g + 1's is free
       issue(min(g + kD - 1, G - 1), ring[(d + kD - 1) % kD]);
       if (g < G) compute(ring[d], g & 1, g);
-      if (g + 1 < G)
-        *reinterpret_cast<uint4*>(a_lds + ((g + 1) & 1) * STAGE + adst) = ring[(d + 1) % kD].a;
+      if (g + 1 < G) stage_a(ring[(d + 1) % kD], (g + 1) & 1);
     }
   }
 
   // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = (r >> 2) * 8 + hf * 4 + (r & 3);
-    const int p = ti.p_begin + m;
-    if (p >= ti.p_end) continue;
-    const float rs = row_scale[m];
-    if (KIND == 0) {
-      if (nvalid[0]) {
-        const int n = ti.nt * 128 + wv * 32 + l32;
-        out[static_cast<size_t>(p) * (N / 2) + n] = silu_mul(acc[0][r] * rs, acc[1][r] * rs);
-      }
-    } else {
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (nvalid[j]) out[static_cast<size_t>(p) * N + nrow[j]] = acc[j][r] * rs;
+    for (int r = 0; r < 16; ++r) {
+      const int m = 32 * i + (r >> 2) * 8 + hf * 4 + (r & 3);
+      const int p = ti.p_begin + m;
+      if (p >= ti.p_end) continue;
+      const float rs = row_scale[m] * 0.0625f;   // the operand codes carry a factor 16
+      if (KIND == 0) {
+        if (nvalid[0]) {
+          const int n = ti.nt * 128 + wv * 32 + l32;
+          out[static_cast<size_t>(p) * (N / 2) + n] =
+              silu_mul(acc[i][0][r] * rs, acc[i][1][r] * rs);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (nvalid[j]) out[static_cast<size_t>(p) * N + nrow[j]] = acc[i][j][r] * rs;
+      }
     }
-  }
 }
 
+// Tile rows: 64 (MT = 2) once the routed rows average a full 32-row tile per
+// active expert, so each expert's weight strip is streamed fewer times.
 template <int KIND>
-hipError_t launch_w4a8_gemm(const int8_t* A, const float* a_scale, const int* a_gsum,
-                            const uint8_t* W, const uint16_t* S, const int* offsets,
-                            const int* sorted_slot, float* out, int K, int N, int E, int topk,
-                            int T, hipStream_t s) {
+hipError_t launch_w4a8_gemm(const int8_t* A, const float* a_scale, const uint8_t* W,
+                            const uint16_t* S, const int* offsets, const int* sorted_slot,
+                            float* out, int K, int N, int E, int topk, int T, hipStream_t s) {
   const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + 255) / 256;
   const long long R = static_cast<long long>(T) * topk;
   const long long act = R < E ? R : E;
-  const long long mt_up = (R + kBM - 1) / kBM + act;
-  long long grid = (mt_up * NT + 7) / 8 * 8;
-  const size_t lds = static_cast<size_t>(kBM) * (K / kGroup) * sizeof(int);
-  hipLaunchKernelGGL((w4a8_mfma_kernel<KIND>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     lds, s, A, a_scale, a_gsum, W, S, offsets, sorted_slot, out, K, N, E, topk,
-                     NT);
+  const bool wide = R >= 32 * act;
+  const int BM = wide ? 64 : 32;
+  const long long mt_up = (R + BM - 1) / BM + act;
+  const dim3 grid(static_cast<unsigned>((mt_up * NT + 7) / 8 * 8));
+  const size_t lds = static_cast<size_t>(256) * (K / kGroup) * 2;   // the tile's scale strips
+  if (wide)
+    hipLaunchKernelGGL((w4a8_mfma_kernel<KIND, 2>), grid, dim3(kThreads), lds, s, A, a_scale, W,
+                       S, offsets, sorted_slot, out, K, N, E, topk, NT);
+  else
+    hipLaunchKernelGGL((w4a8_mfma_kernel<KIND, 1>), grid, dim3(kThreads), lds, s, A, a_scale, W,
+                       S, offsets, sorted_slot, out, K, N, E, topk, NT);
   return hipGetLastError();
 }
 
 struct W4A8Ws {
   int8_t* xq;
   float* xs;
-  int* xg;
   float* h;
   int8_t* hq;
   float* hs;
-  int* hg;
 };
 
 W4A8Ws carve(void* ws, int T, int H, int I, int k) {
@@ -332,15 +395,11 @@ W4A8Ws carve(void* ws, int T, int H, int I, int k) {
   p += align_up(static_cast<size_t>(T) * H, 256);
   w.xs = reinterpret_cast<float*>(p);
   p += align_up(static_cast<size_t>(T) * 4, 256);
-  w.xg = reinterpret_cast<int*>(p);
-  p += align_up(static_cast<size_t>(T) * (H / kGroup) * 4, 256);
   w.h = reinterpret_cast<float*>(p);
   p += align_up(R * I * 4, 256);
   w.hq = reinterpret_cast<int8_t*>(p);
   p += align_up(R * I, 256);
   w.hs = reinterpret_cast<float*>(p);
-  p += align_up(R * 4, 256);
-  w.hg = reinterpret_cast<int*>(p);
   return w;
 }
 
@@ -349,8 +408,7 @@ W4A8Ws carve(void* ws, int T, int H, int I, int k) {
 size_t w4a8_workspace_bytes(int T, int H, int I, int, int k) {
   const size_t R = static_cast<size_t>(T) * k;
   return align_up(static_cast<size_t>(T) * H, 256) + align_up(static_cast<size_t>(T) * 4, 256) +
-         align_up(static_cast<size_t>(T) * (H / kGroup) * 4, 256) + align_up(R * I * 4, 256) +
-         align_up(R * I, 256) + align_up(R * 4, 256) + align_up(R * (I / kGroup) * 4, 256);
+         align_up(R * I * 4, 256) + align_up(R * I, 256) + align_up(R * 4, 256);
 }
 
 hipError_t launch_w4a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
@@ -361,18 +419,18 @@ hipError_t launch_w4a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
   const W4A8Ws w = carve(ws, T, H, I, k);
   const int R = T * k;
   const int rpb = kThreads / kWave;
-  quant_gsum_kernel<uint16_t><<<(T + rpb - 1) / rpb, kThreads, 0, s>>>(x, T, H, w.xq, w.xs, w.xg,
+  quant_rows_kernel<uint16_t><<<(T + rpb - 1) / rpb, kThreads, 0, s>>>(x, T, H, w.xq, w.xs,
                                                                        dbg.xq, dbg.xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_w4a8_gemm<0>(w.xq, w.xs, w.xg, w13, s13, offsets, sorted_slot, w.h, H, 2 * I, E, k,
+  err = launch_w4a8_gemm<0>(w.xq, w.xs, w13, s13, offsets, sorted_slot, w.h, H, 2 * I, E, k,
                             T, s);
   if (err != hipSuccess) return err;
-  quant_gsum_kernel<float><<<(R + rpb - 1) / rpb, kThreads, 0, s>>>(w.h, R, I, w.hq, w.hs, w.hg,
+  quant_rows_kernel<float><<<(R + rpb - 1) / rpb, kThreads, 0, s>>>(w.h, R, I, w.hq, w.hs,
                                                                     dbg.hq, dbg.hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_w4a8_gemm<1>(w.hq, w.hs, w.hg, w2, s2, offsets, sorted_slot, y, I, H, E, k, T, s);
+  return launch_w4a8_gemm<1>(w.hq, w.hs, w2, s2, offsets, sorted_slot, y, I, H, E, k, T, s);
 }
 
 }  // namespace moe

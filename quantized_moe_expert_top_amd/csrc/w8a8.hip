@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
   __shared__ float row_scale[kBM];    // activation scale of each tile row
   __shared__ float col_scale[kW8BN];  // weight scale of each B tile row
   __shared__ int sm_pref[kThreads / kWave];
-  __shared__ int sm_out[3];
+  __shared__ int sm_out[5];
 
   TileInfo ti;
   if (!find_tile<kBM>(offsets, E, NT, sm_pref, sm_out, ti)) return;

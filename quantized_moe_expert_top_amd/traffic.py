@@ -32,7 +32,7 @@ UNIT_KERNELS = {
     "decode_t2": ("moe_layer_w4a16", _LAYER),
     "decode_large": ("moe_layer_w4a16", _LAYER),
     "prefill_t512": ("moe_layer_w4a16", _LAYER),
-    "w4a8_t512": ("moe_grouped_w4a8_ffn", [r"quant_gsum_kernel", r"w4a8_mfma_kernel"]),
+    "w4a8_t512": ("moe_grouped_w4a8_ffn", [r"quant_rows_kernel", r"w4a8_mfma_kernel"]),
     "w8a8_t4096": ("moe_grouped_w8a8_ffn",
                    [r"act_quant_kernel", r"w8a8_mfma_kernel", r"h_quant_kernel"]),
 }

@@ -364,6 +364,9 @@ CUSTOM_W4A8 = [
     ("w4a8_t1", 303, 1, 128, 128, 4, 1),           # one group per row
     ("w4a8_many_rows", 304, 700, 256, 128, 4, 2),  # many 32-row tiles per expert
     ("w4a8_wide", 305, 33, 640, 384, 16, 4),       # partial 256-column down tile
+    ("w4a8_tall", 308, 301, 384, 384, 4, 3),       # 64-row tiles, ragged last tile, 3 groups
+    ("w4a8_k3072", 310, 24, 3072, 256, 8, 2),      # 96 KiB resident tile: one block per CU
+    ("w4a8_deep", 309, 16, 4864, 128, 8, 2),       # 152 KiB tile: activations streamed per group
 ]
 
 
