@@ -1016,6 +1016,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   __shared__ int row_src[BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[5];
+  extern __shared__ uint16_t s_lds[];   // [256][G]: fp16 scales of the tile's weight rows
 
   TileInfo ti;
   if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
@@ -1023,6 +1024,28 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int G = K / kGroup;
+
+  // The scales of the tile's 256 weight rows are contiguous runs of S (two
+  // 128-row strips, gate and up, or one 256-row strip) starting at multiples
+  // of 256 bytes: they are copied to LDS in 16-byte chunks (a per-group load
+  // of one fp16 per row would touch 32 rows per instruction). Rows past the
+  // expert read as 0 through the buffer resource and are never used. Loads
+  // and stores are unconditional (clamped) so all stay in flight together.
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      buffer_rsrc(S + static_cast<size_t>(ti.e) * N * G, static_cast<uint32_t>(N * G) * 2u);
+  constexpr int kScBatch = 4;
+  const int sc_chunks = 32 * G;           // 256 rows * G * 2 bytes / 16
+  const uint32_t strip0 = static_cast<uint32_t>((KIND == 0 ? ti.nt * 128 : ti.nt * 256) * G * 2);
+  const uint32_t strip1 = static_cast<uint32_t>((N / 2 + ti.nt * 128) * G * 2);
+  auto sc_src = [&](int i) -> uint32_t {
+    if (KIND == 0 && i >= 16 * G) return strip1 + (i - 16 * G) * 16;
+    return strip0 + i * 16;
+  };
+  uint4 scv[kScBatch];
+#pragma unroll
+  for (int u = 0; u < kScBatch; ++u)
+    scv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           s_rsrc, sc_src(min(u * kThreads + tid, sc_chunks - 1)), 0, 0));
 
   // source row of each tile row; rows past the expert's block read the first
   // row (their results are dropped)
@@ -1054,15 +1077,26 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   const uint32_t rowb = static_cast<uint32_t>(K / 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * rowb, static_cast<uint32_t>(N) * rowb);
-  const __amdgpu_buffer_rsrc_t s_rsrc =
-      buffer_rsrc(S + static_cast<size_t>(ti.e) * N * G, static_cast<uint32_t>(N * G) * 2u);
-  uint32_t woff[2], soff[2];
+  uint32_t woff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
-    soff[j] = static_cast<uint32_t>(nrow[j] * G) * 2u;
-  }
+  for (int j = 0; j < 2; ++j) woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
+  // this lane's rows within the tile's 256 scale rows
+  int srow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) srow[j] = (KIND == 0) ? j * 128 + wv * 32 + l32 : wv * 64 + j * 32 + l32;
   __syncthreads();
+  // scale strips into LDS (read after the main loop's first barrier)
+  for (int i0 = 0; i0 < sc_chunks; i0 += kScBatch * kThreads) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kScBatch; ++u)
+        scv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               s_rsrc, sc_src(min(i0 + u * kThreads + tid, sc_chunks - 1)), 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kScBatch; ++u)
+      *reinterpret_cast<uint4*>(s_lds + min(i0 + u * kThreads + tid, sc_chunks - 1) * 8) = scv[u];
+  }
 
   // this thread's activation chunks: slot L = tid + 256 v of a stage
   const uint16_t* asrc[CPT];
@@ -1084,7 +1118,6 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
 
   struct Grp {
     uint4 q[2][2];
-    uint32_t sc[2];
     uint4 a[CPT];
   };
   Grp ring[kMfD];
@@ -1098,9 +1131,6 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
     }
 #pragma unroll
     for (int v = 0; v < CPT; ++v) b.a[v] = ld16(asrc[v] + g * kGroup);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, soff[j], g * 2, 0);
   };
   auto stage_a = [&](const Grp& b, int stage) {
 #pragma unroll
@@ -1119,7 +1149,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
       __builtin_bit_cast(bf16x8_t, make_uint4(kBiasPair, kBiasPair, kBiasPair, kBiasPair));
 
   const NibbleConsts nk = nibble_consts();
-  auto compute = [&](const Grp& b, int stage) {
+  auto compute = [&](const Grp& b, int stage, int g) {
     const uint8_t* st = a_lds + stage * STAGE;
     f32x16_t accg[MT][2], cg[MT];
 #pragma unroll
@@ -1137,6 +1167,9 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int s = 0; s < 8; ++s) av[i][s] = *reinterpret_cast<const uint4*>(st + aoffs[i][s]);
+    uint16_t sc_bits[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sc_bits[j] = s_lds[srow[j] * G + g];
     __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the unpack and MFMAs
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -1159,7 +1192,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
     }
     float bs[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bs[j] = fp16_bits_to_f32(static_cast<uint16_t>(b.sc[j]));
+    for (int j = 0; j < 2; ++j) bs[j] = fp16_bits_to_f32(sc_bits[j]);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -1182,7 +1215,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
       const int g = g0 + d;
       __syncthreads();  // group g's stage is written; group g + 1's is free
       issue(min(g + kMfD - 1, G - 1), ring[(d + kMfD - 1) % kMfD]);
-      if (g < G) compute(ring[d], d);
+      if (g < G) compute(ring[d], d, g);
       if (g + 1 < G) stage_a(ring[(d + 1) % kMfD], (d + 1) % kMfD);
     }
   }
@@ -1224,8 +1257,9 @@ hipError_t launch_mfma_t(const uint16_t* A, const uint8_t* W, const uint16_t* S,
   const long long mt_up = (R + BM - 1) / BM + act;
   long long grid = mt_up * NT;
   grid = (grid + 7) / 8 * 8;
+  const size_t lds = static_cast<size_t>(256) * (K / kGroup) * 2;   // the tile's scale strips
   hipLaunchKernelGGL((w4a16_mfma_kernel<KIND, MT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, s, A, W, S, offsets, sorted_slot, out, K, N, E, topk, NT);
+                     dim3(kThreads), lds, s, A, W, S, offsets, sorted_slot, out, K, N, E, topk, NT);
   return hipGetLastError();
 }
 
