@@ -46,6 +46,11 @@ where each function states it:
      w_r[e, h] over the bf16 token rows and the bf16 router rows [E][H] (the
      pages route on such logits; the workload hands them in, and the step that
      makes them is the dense product of the two).
+  R10 expert-load telemetry ("Performance and verification", section "Why it
+     is fast": the engines count their own routing as they run and move the
+     experts used most): a layer's per-expert load is the number of routed
+     rows each expert received; loads add up over calls; the hot list of a
+     layer is its experts by descending load, ties to the lower expert index.
 """
 from __future__ import annotations
 
@@ -286,6 +291,23 @@ def ffn_w4a8(x_bits: np.ndarray, perm: dict, k: int, get_expert) -> dict:
         Y[a:b] = (A2 * fp16_to_f64(s2)[None, :, :]).sum(axis=2) * hs[a:b].astype(np.float64)[:, None]
     out.update(h=h, hq=hq, hs=hs, y=Y)
     return out
+
+
+# --------------------------------------------------------------- telemetry --
+def expert_loads(ids: np.ndarray, E: int) -> np.ndarray:
+    """R10: routed rows per expert of one layer call (int64 [E])."""
+    loads = np.zeros(E, np.int64)
+    for e in np.asarray(ids).ravel():
+        loads[int(e)] += 1
+    return loads
+
+
+def hot_rank(loads: np.ndarray, n: int) -> np.ndarray:
+    """R10: the n experts with the largest load, in descending order of load,
+    ties to the lower expert index (int32 [n])."""
+    loads = np.asarray(loads)
+    order = sorted(range(loads.shape[0]), key=lambda e: (-int(loads[e]), e))
+    return np.asarray(order[:n], np.int32)
 
 
 # ------------------------------------------------------------ whole layer --

@@ -588,3 +588,49 @@ def test_planted_w4a8_zero_point_sign_is_caught():
     e = int(r["ids"][0, 0])
     y = _w4a8_slot_bruteforce(X[0], *get(e), wl.I)
     assert not np.allclose(r["y"][r["perm"]["slot_pos"][0]], y, rtol=1e-6)
+
+
+# --------------------------------------------------------------- telemetry --
+def test_expert_loads_and_hot_rank_hand_fixture():
+    d = gold("hot_rank_hand.json")
+    loads = oracle.expert_loads(np.array(d["ids"]), d["E"])
+    assert loads.tolist() == d["loads"]
+    assert oracle.hot_rank(loads, d["E"]).tolist() == d["hot_all"]
+    assert oracle.hot_rank(loads, 3).tolist() == d["hot_all"][:3]
+    assert oracle.hot_rank(loads, 0).tolist() == []
+
+
+def test_expert_loads_match_permutation_blocks_and_total():
+    """The loads are the lengths of the expert blocks of the stable
+    permutation, and they add up to T * k (every routed row counted once)."""
+    rng = np.random.default_rng(11)
+    for T, E, k in ((1, 4, 1), (37, 16, 3), (300, 128, 8)):
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        loads = oracle.expert_loads(ids, E)
+        assert int(loads.sum()) == T * k
+        off = oracle.permute(ids, E)["expert_offsets"]
+        assert np.array_equal(loads, np.asarray(off[1:]) - np.asarray(off[:-1]))
+
+
+def test_hot_rank_against_repeated_argmax():
+    """A different algorithm: repeatedly take the first maximum and remove it
+    (numpy argmax returns the first, i.e. lowest-index, maximum)."""
+    rng = np.random.default_rng(12)
+    for E in (1, 7, 64, 300):
+        loads = rng.integers(0, 5, size=E)          # a small range: many ties
+        left = loads.astype(np.int64).copy()
+        want = []
+        for _ in range(E):
+            e = int(np.argmax(left))
+            want.append(e)
+            left[e] = -1
+        for n in (0, 1, E // 2, E):
+            assert oracle.hot_rank(loads, n).tolist() == want[:n]
+
+
+def test_planted_hot_rank_tie_order_is_caught():
+    """A copy that breaks ties toward the higher index fails the fixture."""
+    d = gold("hot_rank_hand.json")
+    loads = np.array(d["loads"])
+    bad = sorted(range(len(loads)), key=lambda e: (-int(loads[e]), -e))
+    assert bad != d["hot_all"]
