@@ -218,40 +218,60 @@ def main():
         spread["cold_median_ms_per_step"] = round(float(np.median(cold)), 4)
         spread["warm_ms_per_step"] = round(ms_per_step, 4)
 
+    def time_launches(fn, n=50):
+        """Average device time of fn() over n launches, replayed from a graph
+        (device time, not the host launch rate) unless --eager."""
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        g = None
+        if not args.eager:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(n):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        if g is not None:
+            g.replay()
+        else:
+            for _ in range(n):
+                fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / n
+
     # the router projection ahead of the top-k (logits = x . w_r^T) on this
     # workload's shape, timed alone: a separate row, not part of the step
     wr = torch.from_numpy(synth.router_weights(wl, 0).view(np.int16)).cuda()
     x0 = units[0][0]
     lg = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
-    n_router = 50
-    for _ in range(3):
-        moe.router_logits(x0, wr, lg)
-    torch.cuda.synchronize()
-    rg = None
-    if not args.eager:   # launches replayed from a graph: device time, not host launch rate
-        rg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(rg):
-            for _ in range(n_router):
-                moe.router_logits(x0, wr, lg)
-        rg.replay()
-        torch.cuda.synchronize()
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    if rg is not None:
-        rg.replay()
-    else:
-        for _ in range(n_router):
-            moe.router_logits(x0, wr, lg)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    router_us = r0.elapsed_time(r1) * 1e3 / n_router
+    router_us = time_launches(lambda: moe.router_logits(x0, wr, lg))
     router_bytes = wl.T * wl.H * 2 + wl.E * wl.H * 2 + wl.T * wl.E * 4
     router_row = {"kernel": "router_logits_kernel (moe_router_logits)",
                   "avg_launch_us": round(router_us, 2),
                   "algo_bytes_per_launch": router_bytes,
                   "achieved_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
                   "flops_per_launch": 2 * wl.T * wl.H * wl.E}
+
+    # expert-load telemetry over one step's layers: their expert_offsets
+    # gathered into one [L, E + 1] array, counts accumulated in one launch,
+    # then each layer's 16 most-loaded experts ranked (a separate row)
+    step_units = schedule[0]
+    offs = torch.stack([bufs[u].offsets[:wl.E + 1] for u in step_units])
+    loads = torch.zeros((len(step_units), wl.E), dtype=torch.int64, device="cuda")
+    n_hot = min(16, wl.E)
+    hot = torch.empty((len(step_units), n_hot), dtype=torch.int32, device="cuda")
+    counts_us = time_launches(lambda: moe.expert_counts_accumulate(offs, loads))
+    hot_us = time_launches(lambda: moe.expert_hot_rank(loads, n_hot, hot))
+    telemetry_row = {"kernels": "expert_counts_kernel, hot_rank_kernel "
+                                "(moe_expert_counts_accumulate, moe_expert_hot_rank)",
+                     "layers": len(step_units), "hot_n": n_hot,
+                     "counts_avg_launch_us": round(counts_us, 2),
+                     "hot_rank_avg_launch_us": round(hot_us, 2)}
 
     calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
     eb = expert_bytes(wl)
@@ -323,6 +343,7 @@ def main():
         "cpu_baseline": cpu,
         "spread": spread,
         "router_projection": router_row,
+        "expert_load_telemetry": telemetry_row,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

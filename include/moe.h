@@ -271,6 +271,33 @@ MOE_API int moe_grouped_w4a8_ffn(const moe_shape* shape, const uint16_t* x,
 MOE_API int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w,
                 int32_t T, int32_t H, int32_t k, float* out, void* stream);
 
+/*
+ * moe_expert_counts_accumulate — expert-load telemetry. [PV-fast] (the
+ * engines count their own routing as they run and move the experts used most)
+ * For each layer l < L: counts[l, e] += expert_offsets_l[e+1] - expert_offsets_l[e]
+ * (the routed rows expert e received in that call; moe_permute and
+ * moe_layer_w4a16 write expert_offsets), where expert_offsets_l =
+ * expert_offsets + l * offsets_stride. Exact integer counts.
+ *   expert_offsets int32  [L][offsets_stride] (input; first E+1 of each row used)
+ *   counts         uint64 [L, E] (input/output, owned by the caller; zero it
+ *                                 to start a window)
+ * Requires L >= 0, 1 <= E <= MOE_MAX_EXPERTS, offsets_stride >= E + 1.
+ * Calls that update the same counts must be ordered (one stream).
+ */
+MOE_API int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
+                                 int32_t L, int32_t E, uint64_t* counts, void* stream);
+
+/*
+ * moe_expert_hot_rank — each layer's experts ranked by load. [PV-fast]
+ * hot_ids[l, 0..n) = the n experts with the largest counts[l, :], in
+ * descending order of count, ties broken by the lower expert index (exact).
+ *   counts  uint64 [L, E] (input)
+ *   hot_ids int32  [L, n] (output)
+ * Requires L >= 0, 1 <= E <= MOE_MAX_EXPERTS, 0 <= n <= E.
+ */
+MOE_API int moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n,
+                        int32_t* hot_ids, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

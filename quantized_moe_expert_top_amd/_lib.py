@@ -20,7 +20,8 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_router_lo
            "moe_route_topk",
            "moe_permute_workspace", "moe_permute", "moe_w4a16_workspace",
            "moe_grouped_w4a16_ffn", "moe_w4a8_workspace", "moe_grouped_w4a8_ffn",
-           "moe_w8a8_workspace", "moe_grouped_w8a8_ffn",
+           "moe_w8a8_workspace", "moe_grouped_w8a8_ffn", "moe_expert_counts_accumulate",
+           "moe_expert_hot_rank",
            "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16")
 
 
@@ -71,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),
         "moe_router_logits": (ctypes.c_int, [P, P, I32, I32, I32, P, P]),
+        "moe_expert_counts_accumulate": (ctypes.c_int, [P, ctypes.c_int64, I32, I32, P, P]),
+        "moe_expert_hot_rank": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "moe_route_topk": (ctypes.c_int, [P, I32, I32, I32, P, P, P]),
         "moe_permute_workspace": (SZ, [I32, I32, I32]),
         "moe_permute": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
@@ -140,6 +143,29 @@ def router_logits(x, w_router, logits, stream=None) -> None:
     _need(logits, T * E * 4, "logits")
     _check("moe_router_logits", load().moe_router_logits(_ptr(x), _ptr(w_router), T, H, E,
                                                          _ptr(logits), _stream(stream)))
+
+
+def expert_counts_accumulate(expert_offsets, counts, stream=None) -> None:
+    """counts [L, E] uint64 (int64 tensor) += per-expert rows of each layer's
+    expert_offsets [L, stride >= E + 1] (or [E + 1] with counts [E])."""
+    L, E = (1, counts.shape[0]) if counts.dim() == 1 else tuple(counts.shape)
+    stride = expert_offsets.shape[-1] if expert_offsets.dim() > 1 else E + 1
+    if L > 0:
+        _need(expert_offsets, ((L - 1) * stride + E + 1) * 4, "expert_offsets")
+        _need(counts, L * E * 8, "counts")
+    _check("moe_expert_counts_accumulate", load().moe_expert_counts_accumulate(
+        _ptr(expert_offsets), stride, L, E, _ptr(counts), _stream(stream)))
+
+
+def expert_hot_rank(counts, n: int, hot_ids, stream=None) -> None:
+    """hot_ids [L, n] int32 = each layer's n most-loaded experts (descending,
+    ties to the lower index) from counts [L, E] (or [E] with hot_ids [n])."""
+    L, E = (1, counts.shape[0]) if counts.dim() == 1 else tuple(counts.shape)
+    if L > 0 and n > 0:
+        _need(counts, L * E * 8, "counts")
+        _need(hot_ids, L * n * 4, "hot_ids")
+    _check("moe_expert_hot_rank", load().moe_expert_hot_rank(_ptr(counts), L, E, n, _ptr(hot_ids),
+                                                             _stream(stream)))
 
 
 def route_topk(logits, k: int, topk_ids, topk_w, stream=None) -> None:

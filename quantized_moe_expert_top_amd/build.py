@@ -17,7 +17,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
 SOURCES = ["api.cpp", "router.hip", "route.hip", "permute.hip", "w4a16.hip", "w4a8.hip",
-           "w8a8.hip", "combine.hip"]
+           "w8a8.hip", "combine.hip", "telemetry.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -344,4 +344,36 @@ int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w, in
                   "moe_combine launch");
 }
 
+int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
+                                 int32_t L, int32_t E, uint64_t* counts, void* stream) {
+  if (L < 0) return fail(MOE_EINVAL, "L = %d < 0", L);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  if (offsets_stride < static_cast<int64_t>(E) + 1)
+    return fail(MOE_ESHAPE, "offsets_stride = %lld < E + 1", static_cast<long long>(offsets_stride));
+  if (L == 0) return MOE_OK;
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(counts);
+  int st;
+  if ((st = check_device())) return st;
+  return launched(moe::launch_expert_counts(expert_offsets, offsets_stride, L, E,
+                                            reinterpret_cast<unsigned long long*>(counts),
+                                            static_cast<hipStream_t>(stream)),
+                  "moe_expert_counts_accumulate launch");
+}
+
+int moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n, int32_t* hot_ids,
+                        void* stream) {
+  if (L < 0) return fail(MOE_EINVAL, "L = %d < 0", L);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  if (n < 0 || n > E) return fail(MOE_ESHAPE, "n = %d outside [0, E = %d]", n, E);
+  if (L == 0 || n == 0) return MOE_OK;
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(hot_ids);
+  int st;
+  if ((st = check_device())) return st;
+  return launched(moe::launch_hot_rank(reinterpret_cast<const unsigned long long*>(counts), L, E, n,
+                                       hot_ids, static_cast<hipStream_t>(stream)),
+                  "moe_expert_hot_rank launch");
+}
+
 }  // extern "C"

@@ -60,6 +60,10 @@ hipError_t launch_w4a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
                            const uint16_t* s2, const int* offsets, const int* sorted_slot,
                            float* y, const W4A8Debug& dbg, void* ws, hipStream_t s);
 
+hipError_t launch_expert_counts(const int* offsets, long long stride, int L, int E,
+                                unsigned long long* counts, hipStream_t s);
+hipError_t launch_hot_rank(const unsigned long long* counts, int L, int E, int n, int* hot,
+                           hipStream_t s);
 hipError_t launch_combine(const float* y, const int* slot_pos, const float* w, int T, int H,
                           int k, float* out, hipStream_t s);
 

@@ -32,7 +32,7 @@ def header_functions():
 @needs_lib
 def test_exports_match_header():
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(LIB, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -222,3 +222,24 @@ def test_router_logits_validation(args, status):
     assert LIB.moe_router_logits(*args, None) == status
     if status:
         assert LIB.moe_last_error()
+
+
+@needs_lib
+def test_expert_telemetry_validation():
+    f = LIB.moe_expert_counts_accumulate
+    assert f(A, 9, -1, 8, A, None) == 1                  # L < 0
+    assert f(A, 9, 2, 0, A, None) == 2                   # E < 1
+    assert f(A, 9, 2, 1025, A, None) == 2                # E > MOE_MAX_EXPERTS
+    assert f(A, 8, 2, 8, A, None) == 2                   # stride < E + 1
+    assert f(None, 9, 0, 8, None, None) == 0             # nothing to do
+    assert f(None, 9, 2, 8, A, None) == 1
+    assert f(A, 9, 2, 8, MIS, None) == 3
+    h = LIB.moe_expert_hot_rank
+    assert h(A, 1, 8, 9, A, None) == 2                   # n > E
+    assert h(A, 1, 8, -1, A, None) == 2
+    assert h(A, -1, 8, 2, A, None) == 1
+    assert h(None, 3, 8, 0, None, None) == 0             # n = 0: nothing to do
+    assert h(A, 3, 8, 2, None, None) == 1
+    if _no_gpu():
+        assert f(A, 9, 2, 8, A, None) == 6
+        assert h(A, 3, 8, 2, A, None) == 6

@@ -578,3 +578,64 @@ def test_router_logits_deterministic():
     moe.router_logits(x, wr, b)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
+
+
+# --------------------------------------------------------------- telemetry --
+def test_expert_counts_accumulate_over_layers_and_steps():
+    """Counts from the device permutation of several layers over four steps,
+    one launch per step over a strided [L][E + 3] offsets array; the counters
+    start above 2^32 so a 32-bit add would show."""
+    import quantized_moe_expert_top_amd as moe
+    E, L = 128, 3
+    shapes = [(2, 8, 0.0), (512, 8, 1.1), (37, 4, 0.0)]
+    base = np.int64(2 ** 33 - 5)
+    want = np.full((L, E), base, np.int64)
+    counts = torch.full((L, E), int(base), dtype=torch.int64, device="cuda")
+    offs = torch.full((L, E + 3), -9, dtype=torch.int32, device="cuda")
+    for step in range(4):
+        for l, (T, k, skew) in enumerate(shapes):
+            ids = _random_ids(T, E, k, seed=1000 * step + l, skew=skew)
+            p = _permute_gpu(ids, E)
+            offs[l, :E + 1] = to_dev(p["expert_offsets"].astype(np.int32))
+            want[l] += oracle.expert_loads(ids, E)
+        _say("expert counts step", step)
+        moe.expert_counts_accumulate(offs, counts)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(counts), want)
+
+
+def test_expert_counts_from_the_layer_entry():
+    """The offsets moe_layer_w4a16 writes feed the counters directly."""
+    import quantized_moe_expert_top_amd as moe
+    wl = synth.workload("decode_t2")
+    counts = torch.zeros(wl.E, dtype=torch.int64, device="cuda")
+    want = np.zeros(wl.E, np.int64)
+    for u in range(3):
+        x, L = synth.x_bf16(wl, u), synth.router_logits(wl, u)
+        b = moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, "w4a16")
+        ids, _ = oracle.route_topk(L, wl.k)
+        wts = stage_weights(wl, u, np.unique(ids))
+        moe.moe_layer(b, to_dev(x), to_dev(L), wts)
+        moe.expert_counts_accumulate(b.offsets, counts)
+        want += oracle.expert_loads(ids, wl.E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(counts), want)
+
+
+@pytest.mark.parametrize("E", [1, 8, 128, 256, 1024])
+def test_expert_hot_rank_matches_oracle(E):
+    """Many ties (a small value range) in both 32-bit halves of the counts."""
+    import quantized_moe_expert_top_amd as moe
+    rng = np.random.default_rng(E)
+    L = 3
+    c = (rng.integers(0, 3, size=(L, E)).astype(np.uint64) << np.uint64(32)) + \
+        rng.integers(0, 4, size=(L, E)).astype(np.uint64)
+    counts = to_dev(c.view(np.int64))
+    for n in sorted({1, max(E // 2, 1), E}):
+        hot = torch.full((L, n), -5, dtype=torch.int32, device="cuda")
+        _say("hot rank", E, n)
+        moe.expert_hot_rank(counts, n, hot)
+        torch.cuda.synchronize()
+        got = to_np(hot)
+        for l in range(L):
+            np.testing.assert_array_equal(got[l], oracle.hot_rank(c[l], n))
