@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 // atomics cross blocks.
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
-constexpr int kDecodeBlocks = 256;   // target blocks of the down kernel
+constexpr int kDecodeBlocks = 512;   // target blocks of the down kernel (2 per CU)
 constexpr int kDecodeGateupBlocks = 512;     // working blocks of the persistent gate/up (2 per CU)
 constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
 
@@ -667,6 +667,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   float* bsum = reinterpret_cast<float*>(lds + R * (I / 2));     // [R][C]
   float* ybuf = bsum + R * C;                                    // [R][nr]
   __shared__ int s_e[kDecodeMaxR], s_p0[kDecodeMaxR], s_m[kDecodeMaxR];
+  __shared__ float s_w[kDecodeMaxR];
+  __shared__ int s_sp[kDecodeMaxR];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int lg = wv * G + lane / LK, lk = lane % LK;
   const int u0 = blockIdx.x * upb;                 // first unit (row pair) of the tile
@@ -703,6 +705,14 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   const int n_stage = R * C;
   StageRegs h0;
   gemv_stage_load(h, R, I, tid, h0);
+  // the combine's weights and slot positions were written before this kernel
+  // started: request them now, park them in LDS once the h stage has landed
+  float my_w = 0.0f;
+  int my_sp = 0;
+  if (tid < R) {
+    my_w = topk_w[tid];
+    my_sp = slot_pos[tid];
+  }
   const int act = R < E ? R : E;
   const int na = rec[0];
   auto first_codes = [&](int q, Item& w) {
@@ -718,6 +728,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     s_m[i] = rec[3 + 3 * i];
   }
   gemv_stage_store(R, I, tid, h0, xs, bsum);
+  if (tid < R) {
+    s_w[tid] = my_w;
+    s_sp[tid] = my_sp;
+  }
   for (int i0 = tid + 2 * kThreads; i0 < n_stage; i0 += 2 * kThreads) {
     StageRegs r;
     gemv_stage_load(h, R, I, i0, r);
@@ -783,10 +797,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const int n = 2 * u0 + r;
     if (n >= H) continue;
     float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float wj = topk_w[t * k + j];
-      acc += wj * ybuf[slot_pos[t * k + j] * nr + r];
-    }
+    for (int j = 0; j < k; ++j) acc += s_w[t * k + j] * ybuf[s_sp[t * k + j] * nr + r];
     out[static_cast<size_t>(t) * H + n] = acc;
   }
 }
