@@ -37,7 +37,8 @@
  *   - Numerics are deterministic: integer atomics only (counts, maxima), no
  *     float atomics; two runs on the same inputs give identical bits.
  *   - T = 0 is a valid empty batch. T*k*max(H, I) and 2*H*I must stay below
- *     2^31 (32-bit element offsets).
+ *     2^31 (32-bit element offsets); H and I are at most MOE_MAX_DIM (a grouped
+ *     GEMM block holds the scales of its 256 weight rows in LDS).
  *   - Out-of-range expert ids or non-finite logits are outside the contract.
  */
 #ifndef MOE_H
@@ -60,6 +61,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 #define MOE_GROUP 128
+#define MOE_MAX_DIM 16384   /* largest H and I of the FFN and layer calls */
 
 typedef enum {
   MOE_OK = 0,

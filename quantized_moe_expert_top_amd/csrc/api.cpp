@@ -72,6 +72,8 @@ int check_shape(const moe_shape* s, int hmod, int imod) {
   if (st) return st;
   if (s->H < hmod || s->H % hmod) return fail(MOE_ESHAPE, "H = %d must be a positive multiple of %d", s->H, hmod);
   if (s->I < imod || s->I % imod) return fail(MOE_ESHAPE, "I = %d must be a positive multiple of %d", s->I, imod);
+  if (s->H > MOE_MAX_DIM || s->I > MOE_MAX_DIM)
+    return fail(MOE_ESHAPE, "H = %d or I = %d above %d", s->H, s->I, MOE_MAX_DIM);
   const long long hi = s->H > s->I ? s->H : s->I;
   if (static_cast<long long>(s->T) * s->k * hi >= (1LL << 31))
     return fail(MOE_ESHAPE, "T*k*max(H, I) = %lld too large for 32-bit offsets",

@@ -106,6 +106,7 @@ def test_w4a16_validation():
     assert f(ctypes.byref(_shape(H=200)), *ok, A, need, None) == 2     # H % 128
     assert f(ctypes.byref(_shape(I=64)), *ok, A, need, None) == 2      # I % 128
     assert f(ctypes.byref(_shape(k=9)), *ok, A, need, None) == 2
+    assert f(ctypes.byref(_shape(I=16512)), *ok, A, need, None) == 2        # I > MOE_MAX_DIM
     assert f(None, *ok, A, need, None) == 1
     assert f(ctypes.byref(s), *ok, A, need - 1, None) == 4
     bad = list(ok)
@@ -130,6 +131,7 @@ def test_w4a8_validation():
     assert f(ctypes.byref(_shape(H=192)), *ok, None, A, need, None) == 2     # H % 128
     assert f(ctypes.byref(_shape(I=64)), *ok, None, A, need, None) == 2      # I % 128
     assert f(ctypes.byref(_shape(k=9)), *ok, None, A, need, None) == 2
+    assert f(ctypes.byref(_shape(H=16512)), *ok, None, A, need, None) == 2   # H > MOE_MAX_DIM
     assert f(None, *ok, None, A, need, None) == 1
     assert f(ctypes.byref(s), *ok, None, A, need - 1, None) == 4
     bad = list(ok)
