@@ -6,13 +6,14 @@
 //      rint(x/s) clamped to [-127, 127]. The GEMM operand copy holds each
 //      8-code chunk in the order {0,2,4,6,1,3,5,7} (the order the weight
 //      unpacking below produces); the debug copy is in natural order.
-//   2. gate/up: v_mfma_i32_32x32x32_i8 over (expert, 32-row, 128 h-column)
-//      tiles. A code c becomes the int8 16*(c - 8): the nibble xor 8 (its
-//      two's complement 4-bit value) placed in the high half of a byte, so
-//      the integer dot of a 128-k group is exact and needs no zero-point
-//      correction; each group's dot is scaled by the group's fp16 scale and
-//      accumulated in float32; the epilogue applies row scale / 16 (exact)
-//      and SwiGLU, writing h float32 in grouped order.
+//   2. gate/up: v_mfma_i32_32x32x32_i8 over (expert, 32- or 64-row,
+//      128 h-column) tiles. A code c becomes the int8 16*(c - 8): the nibble
+//      xor 8 (its two's complement 4-bit value) placed in the high half of a
+//      byte, so the integer dot of a 128-k group is exact and needs no
+//      zero-point correction; each group's dot is scaled by the group's fp16
+//      scale (the tile's scales are staged in LDS) and accumulated in
+//      float32; the epilogue applies row scale / 16 (exact) and SwiGLU,
+//      writing h float32 in grouped order.
 //   3. h quant: step 1 on h, one row per routed slot.
 //   4. down: step 2 on hq against W2; y = hs/16 * acc, float32.
 #include "common.h"
