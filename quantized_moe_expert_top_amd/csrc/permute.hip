@@ -6,12 +6,14 @@
 // batch's rows grouped per expert). Integer work only, so every output is
 // exact and deterministic (integer LDS atomics for the counts, nothing else).
 //
-// Stability inside a 256-slot round comes from a wave-level "match": lanes
-// holding the same expert id are found with one ballot per id bit; a lane's
-// rank is the number of matching lanes below it, and per-wave counts kept in
-// LDS order the four waves of the block. Chunks of 1024 slots are handled by
-// one block each; a block's base per expert is the count of that expert in
-// all earlier chunks (a column prefix sum over the per-chunk histograms).
+// Stability inside a round of one slot per thread comes from a wave-level
+// "match": lanes holding the same expert id are found with one ballot per id
+// bit; a lane's rank is the number of matching lanes below it, and per-wave
+// counts kept in LDS order the waves of the block. Up to 8192 slots (E <= 512)
+// one block of 1024 threads does everything in one launch; beyond that,
+// chunks of 1024 slots are handled by one block each, and a block's base per
+// expert is the count of that expert in all earlier chunks (a column prefix
+// sum over the per-chunk histograms).
 #include "common.h"
 #include "launch.h"
 
@@ -48,8 +50,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Block-wide exclusive scan of one value per thread (256 threads).
-__device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total) {
+// Block-wide exclusive scan of one value per thread (NTHR threads).
+template <int NTHR>
+__device__ __forceinline__ int block_excl_scan_n(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) wave_tot[w] = incl;
@@ -57,7 +60,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total)
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NTHR / kWave; ++i) {
     const int t = wave_tot[i];
     if (i < w) before += t;
     total += t;
@@ -68,9 +71,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total)
 
 // counts[e] (LDS) -> offsets (global, [E+1]) and run[e] (LDS, = offsets[e]);
 // the active list and its length.
+template <int NTHR>
 __device__ void offsets_and_active(const int* counts, int* run, int E, int R, int* wave_tot,
                                    int* offsets, int* active, int* n_active) {
-  const int ept = (E + kThreads - 1) / kThreads;  // <= 4
+  const int ept = (E + NTHR - 1) / NTHR;  // <= 4
   const int e0 = threadIdx.x * ept;
   int c[4], f[4], sc = 0, sf = 0;
 #pragma unroll
@@ -82,8 +86,8 @@ __device__ void offsets_and_active(const int* counts, int* run, int E, int R, in
     sf += f[i];
   }
   int tot_c, tot_f;
-  int oc = block_excl_scan(sc, wave_tot, tot_c);
-  int of = block_excl_scan(sf, wave_tot, tot_f);
+  int oc = block_excl_scan_n<NTHR>(sc, wave_tot, tot_c);
+  int of = block_excl_scan_n<NTHR>(sf, wave_tot, tot_f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + i;
@@ -101,18 +105,44 @@ __device__ void offsets_and_active(const int* counts, int* run, int E, int R, in
   }
 }
 
-// Stable scatter of slots [base, base + kChunk) given run[e] = first free
-// grouped position of expert e. wc[kWaves * E] must be zero on entry and is
-// left zero.
-__device__ void scatter_chunk(const int* __restrict__ ids, int R, int E, int nbits, int base,
-                              int* run, int* wc, int* __restrict__ sorted_slot,
-                              int* __restrict__ slot_pos) {
+// The ids of slots base + r * NTHR + tid, r < MAXR, as sort keys (E past the
+// end of [base, R)), loaded together (clamped addresses, no branches) so
+// their latencies overlap. With no slot at or after base (an empty batch,
+// where ids may be NULL) nothing is read.
+template <int NTHR, int MAXR>
+__device__ __forceinline__ void load_keys(const int* __restrict__ ids, int R, int E, int base,
+                                          uint32_t (&keys)[MAXR]) {
+  if (base >= R) {   // uniform across the block
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) keys[r] = static_cast<uint32_t>(E);
+    return;
+  }
+  int raw[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) raw[r] = ids[min(base + r * NTHR + static_cast<int>(threadIdx.x), R - 1)];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int f = base + r * NTHR + threadIdx.x;
+    keys[r] = f < R ? static_cast<uint32_t>(clamp_id(raw[r], E)) : static_cast<uint32_t>(E);
+  }
+}
+
+// Stable scatter of slots base + r * NTHR + tid (r < MAXR, slot < R) in
+// rounds of NTHR, given their keys and run[e] = first free grouped position
+// of expert e. wc[NTHR / 64 * E] must be zero on entry and is left zero.
+template <int NTHR, int MAXR>
+__device__ void scatter_keys(const uint32_t (&keys)[MAXR], int R, int E, int nbits, int base,
+                             int* run, int* wc, int* __restrict__ sorted_slot,
+                             int* __restrict__ slot_pos) {
+  constexpr int NW = NTHR / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int r = 0; r < kChunk / kThreads; ++r) {
-    const int f = base + r * kThreads + tid;
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    if (base + r * NTHR >= R) break;   // uniform across the block
+    const int f = base + r * NTHR + tid;
     const bool valid = f < R;
-    const uint32_t key = valid ? static_cast<uint32_t>(clamp_id(ids[f], E)) : static_cast<uint32_t>(E);
+    const uint32_t key = keys[r];
     const uint64_t m = wave_match(key, nbits);
     const int rank = __popcll(m & below);
     const bool leader = rank == 0;
@@ -121,7 +151,7 @@ __device__ void scatter_chunk(const int* __restrict__ ids, int R, int E, int nbi
     int pre = 0, tot = 0;
     if (valid) {
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
+      for (int v = 0; v < NW; ++v) {
         const int c = wc[v * E + key];
         if (v < w) pre += c;
         tot += c;
@@ -141,23 +171,30 @@ __device__ void scatter_chunk(const int* __restrict__ ids, int R, int E, int nbi
 
 __device__ __forceinline__ int id_bits(int E) { return 32 - __clz(E); }  // covers 0..E
 
-// R <= kChunk: everything in one block.
-__global__ __launch_bounds__(kThreads) void permute_small_kernel(
+// Everything in one block of NTHR threads (R <= kChunk with 256 threads, up
+// to kSingleMaxR with 1024): one launch instead of three.
+template <int NTHR, int MAXR>
+__global__ __launch_bounds__(NTHR) void permute_small_kernel(
     const int* __restrict__ ids, int R, int E, int* __restrict__ offsets,
     int* __restrict__ sorted_slot, int* __restrict__ slot_pos, int* __restrict__ active,
     int* __restrict__ n_active) {
+  constexpr int NW = NTHR / kWave;
   extern __shared__ int sm[];
   int* counts = sm;            // [E]
   int* run = counts + E;       // [E]
-  int* wc = run + E;           // [kWaves * E]
-  __shared__ int wave_tot[kWaves];
-  for (int i = threadIdx.x; i < (2 + kWaves) * E; i += kThreads) sm[i] = 0;
+  int* wc = run + E;           // [NW * E]
+  __shared__ int wave_tot[NW];
+  uint32_t keys[MAXR];         // every slot's id is read from memory once
+  load_keys<NTHR, MAXR>(ids, R, E, 0, keys);
+  for (int i = threadIdx.x; i < (2 + NW) * E; i += NTHR) sm[i] = 0;
   __syncthreads();
-  for (int f = threadIdx.x; f < R; f += kThreads) atomicAdd(&counts[clamp_id(ids[f], E)], 1);
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r)
+    if (keys[r] < static_cast<uint32_t>(E)) atomicAdd(&counts[keys[r]], 1);
   __syncthreads();
-  offsets_and_active(counts, run, E, R, wave_tot, offsets, active, n_active);
+  offsets_and_active<NTHR>(counts, run, E, R, wave_tot, offsets, active, n_active);
   __syncthreads();
-  scatter_chunk(ids, R, E, id_bits(E), 0, run, wc, sorted_slot, slot_pos);
+  scatter_keys<NTHR, MAXR>(keys, R, E, id_bits(E), 0, run, wc, sorted_slot, slot_pos);
 }
 
 __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int* __restrict__ ids,
@@ -207,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void permute_scan_kernel(
     counts[e] = acc;
   }
   __syncthreads();
-  offsets_and_active(counts, run, E, R, wave_tot, offsets, active, n_active);
+  offsets_and_active<kThreads>(counts, run, E, R, wave_tot, offsets, active, n_active);
 }
 
 __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
@@ -221,14 +258,25 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
     run[e] = offsets[e] + bases[static_cast<size_t>(blockIdx.x) * E + e];
   for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wc[i] = 0;
   __syncthreads();
-  scatter_chunk(ids, R, E, id_bits(E), blockIdx.x * kChunk, run, wc, sorted_slot, slot_pos);
+  uint32_t keys[kChunk / kThreads];
+  load_keys<kThreads, kChunk / kThreads>(ids, R, E, blockIdx.x * kChunk, keys);
+  scatter_keys<kThreads, kChunk / kThreads>(keys, R, E, id_bits(E), blockIdx.x * kChunk, run, wc,
+                                            sorted_slot, slot_pos);
 }
 
 }  // namespace
 
+// the one-block path at 1024 threads: R <= kSingleMaxR and E <= kSingleMaxE
+// (its LDS, (2 + 16) * E ints, stays within 64 KiB)
+constexpr int kSingleMaxR = 8192;
+constexpr int kSingleMaxE = 512;
+static bool single_block(long long R, int E) {
+  return R <= kChunk || (R <= kSingleMaxR && E <= kSingleMaxE);
+}
+
 size_t permute_workspace_bytes(int T, int E, int k) {
   const long long R = static_cast<long long>(T) * k;
-  if (R <= kChunk) return 0;
+  if (single_block(R, E)) return 0;
   const long long NB = (R + kChunk - 1) / kChunk;
   return static_cast<size_t>(2 * NB * E) * sizeof(int);
 }
@@ -238,8 +286,14 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* offsets, int
   const int R = T * k;
   if (R <= kChunk) {
     const size_t lds = static_cast<size_t>(2 + kWaves) * E * sizeof(int);
-    permute_small_kernel<<<1, kThreads, lds, s>>>(ids, R, E, offsets, sorted_slot, slot_pos,
-                                                  active, n_active);
+    permute_small_kernel<kThreads, kChunk / kThreads><<<1, kThreads, lds, s>>>(
+        ids, R, E, offsets, sorted_slot, slot_pos, active, n_active);
+    return hipGetLastError();
+  }
+  if (single_block(R, E)) {
+    const size_t lds = static_cast<size_t>(2 + 1024 / kWave) * E * sizeof(int);
+    permute_small_kernel<1024, kSingleMaxR / 1024><<<1, 1024, lds, s>>>(
+        ids, R, E, offsets, sorted_slot, slot_pos, active, n_active);
     return hipGetLastError();
   }
   const int NB = (R + kChunk - 1) / kChunk;
