@@ -257,6 +257,7 @@ CUSTOM_W8 = [
     ("w8_ragged", 202, 45, 192, 320, 6, 3),   # K=192/320: not multiples of 128
     ("w8_t1", 203, 1, 128, 64, 4, 1),
     ("w8_many_rows", 204, 700, 256, 128, 4, 2),   # >128 rows per expert
+    ("w8_e1024", 206, 40, 256, 128, 1024, 32),    # most experts hold one row
 ]
 
 
@@ -367,7 +368,8 @@ CUSTOM_W4A8 = [
     ("w4a8_wide", 305, 33, 640, 384, 16, 4),       # partial 256-column down tile
     ("w4a8_tall", 308, 301, 384, 384, 4, 3),       # 64-row tiles, ragged last tile, 3 groups
     ("w4a8_k3072", 310, 24, 3072, 256, 8, 2),      # 96 KiB resident tile: one block per CU
-    ("w4a8_deep", 309, 16, 4864, 128, 8, 2),       # 152 KiB tile: activations streamed per group
+    ("w4a8_deep", 309, 16, 4864, 128, 8, 2),       # long K: many groups per tile
+    ("w4a8_e1024", 311, 40, 256, 128, 1024, 32),   # most experts hold one row
 ]
 
 
@@ -540,6 +542,8 @@ ROUTER_CASES = [
     ("router_ragged", 402, 45, 192, 40),      # partial token and expert tiles
     ("router_prefill", 403, 512, 2048, 128),
     ("router_large", 404, 2, 7168, 256),
+    ("router_e1024_few", 405, 7, 256, 1024),    # the few-token path at the largest E
+    ("router_e1024", 407, 40, 256, 1024),       # the MFMA path at the largest E
 ]
 
 
