@@ -55,7 +55,23 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 }
 
 // One wave per row of K values (bf16 x rows or float32 h rows), K % 128 == 0.
-// Lane l takes 8-value chunks l, l + 64, ...
+// Lane l takes 8-value chunks l, l + 64, ... A row of at most kRowChunks
+// chunks per lane stays in registers between the absmax and the coding pass
+// (one read of memory); longer rows are read twice.
+constexpr int kRowChunks = 4;
+
+__device__ __forceinline__ void code_chunk(const float (&v)[8], float s, int8_t* q, int8_t* dbg_q) {
+  uint32_t nat[2] = {0, 0}, op[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = static_cast<uint32_t>(quant_code4a8(v[i], s)) & 0xFFu;
+    nat[i >> 2] |= b << (8 * (i & 3));
+    op[i & 1] |= b << (8 * (i >> 1));   // even k in dword 0, odd k in dword 1
+  }
+  *reinterpret_cast<uint2*>(q) = make_uint2(op[0], op[1]);
+  if (dbg_q) *reinterpret_cast<uint2*>(dbg_q) = make_uint2(nat[0], nat[1]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T* __restrict__ src, int rows,
                                                               int K, int8_t* __restrict__ q,
@@ -67,7 +83,32 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T* __restric
   if (r >= rows) return;  // uniform per wave
   const T* row = src + static_cast<size_t>(r) * K;
   const int C = K / 8;
+  int8_t* qrow = q + static_cast<size_t>(r) * K;
+  int8_t* drow = dbg_q ? dbg_q + static_cast<size_t>(r) * K : nullptr;
   float amax = 0.0f;
+  if (C <= kRowChunks * kWave) {   // uniform: the row stays in registers
+    float v[kRowChunks][8];
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) load8(row + min(lane + i * kWave, C - 1) * 8, v[i]);
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i)
+      if (lane + i * kWave < C)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
+    const float s = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) {
+      const int c = lane + i * kWave;
+      if (c < C) code_chunk(v[i], s, qrow + c * 8, drow ? drow + c * 8 : nullptr);
+    }
+    if (lane == 0) {
+      scale[r] = s;
+      if (dbg_s) dbg_s[r] = s;
+    }
+    return;
+  }
   for (int c = lane; c < C; c += kWave) {
     float v[8];
     load8(row + c * 8, v);
@@ -80,16 +121,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const T* __restric
   for (int c = lane; c < C; c += kWave) {
     float v[8];
     load8(row + c * 8, v);
-    uint32_t nat[2] = {0, 0}, op[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = static_cast<uint32_t>(quant_code4a8(v[i], s)) & 0xFFu;
-      nat[i >> 2] |= b << (8 * (i & 3));
-      op[i & 1] |= b << (8 * (i >> 1));   // even k in dword 0, odd k in dword 1
-    }
-    *reinterpret_cast<uint2*>(q + static_cast<size_t>(r) * K + c * 8) = make_uint2(op[0], op[1]);
-    if (dbg_q)
-      *reinterpret_cast<uint2*>(dbg_q + static_cast<size_t>(r) * K + c * 8) = make_uint2(nat[0], nat[1]);
+    code_chunk(v, s, qrow + c * 8, drow ? drow + c * 8 : nullptr);
   }
   if (lane == 0) {
     scale[r] = s;

@@ -32,6 +32,38 @@ __device__ __forceinline__ int8_t quant_code(float v, float s) {
 }
 
 // One wave per token row of x (bf16 [T, H]); H % 8 == 0.
+// One wave per row. A row of at most kRowChunks chunks per lane stays in
+// registers between the absmax and the coding pass (one read of memory);
+// longer rows are read twice.
+constexpr int kRowChunks = 4;
+
+__device__ __forceinline__ uint2 code_bf16x8(const uint4& v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = static_cast<uint8_t>(quant_code(bf16lo(w[i]), s));
+    const uint32_t hi = static_cast<uint8_t>(quant_code(bf16hi(w[i]), s));
+    packed[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+__device__ __forceinline__ float amax_bf16x8(const uint4& v, float amax) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(w[i])), fabsf(bf16hi(w[i]))));
+  return amax;
+}
+__device__ __forceinline__ uint32_t code_f32x4(const float4& v, float s) {
+  return static_cast<uint8_t>(quant_code(v.x, s)) |
+         (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.y, s))) << 8) |
+         (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.z, s))) << 16) |
+         (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.w, s))) << 24);
+}
+__device__ __forceinline__ float amax_f32x4(const float4& v, float amax) {
+  return fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+}
+
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x,
                                                              int T, int H,
                                                              int8_t* __restrict__ xq,
@@ -42,30 +74,43 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
   const uint16_t* row = x + static_cast<size_t>(t) * H;
+  int8_t* qrow = xq + static_cast<size_t>(t) * H;
+  int8_t* drow = dbg_xq ? dbg_xq + static_cast<size_t>(t) * H : nullptr;
+  const int C = H / 8;   // 16-byte chunks of 8 values
   float amax = 0.0f;
-  for (int c = lane * 8; c < H; c += kWave * 8) {
-    const uint4 v = ld16(row + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (C <= kRowChunks * kWave) {   // uniform: the row stays in registers
+    uint4 v[kRowChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      amax = fmaxf(amax, fmaxf(fabsf(bf16lo(w[i])), fabsf(bf16hi(w[i]))));
+    for (int i = 0; i < kRowChunks; ++i) v[i] = ld16(row + min(lane + i * kWave, C - 1) * 8);
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i)
+      if (lane + i * kWave < C) amax = amax_bf16x8(v[i], amax);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
+    const float s = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) {
+      const int c = lane + i * kWave;
+      if (c < C) {
+        const uint2 pv = code_bf16x8(v[i], s);
+        *reinterpret_cast<uint2*>(qrow + c * 8) = pv;
+        if (drow) *reinterpret_cast<uint2*>(drow + c * 8) = pv;
+      }
+    }
+    if (lane == 0) {
+      xs[t] = s;
+      if (dbg_xs) dbg_xs[t] = s;
+    }
+    return;
   }
+  for (int c = lane; c < C; c += kWave) amax = amax_bf16x8(ld16(row + c * 8), amax);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
   const float s = amax / 127.0f;
-  for (int c = lane * 8; c < H; c += kWave * 8) {
-    const uint4 v = ld16(row + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = static_cast<uint8_t>(quant_code(bf16lo(w[i]), s));
-      const uint32_t hi = static_cast<uint8_t>(quant_code(bf16hi(w[i]), s));
-      packed[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-    }
-    const uint2 pv = make_uint2(packed[0], packed[1]);
-    *reinterpret_cast<uint2*>(xq + static_cast<size_t>(t) * H + c) = pv;
-    if (dbg_xq) *reinterpret_cast<uint2*>(dbg_xq + static_cast<size_t>(t) * H + c) = pv;
+  for (int c = lane; c < C; c += kWave) {
+    const uint2 pv = code_bf16x8(ld16(row + c * 8), s);
+    *reinterpret_cast<uint2*>(qrow + c * 8) = pv;
+    if (drow) *reinterpret_cast<uint2*>(drow + c * 8) = pv;
   }
   if (lane == 0) {
     xs[t] = s;
@@ -73,7 +118,6 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   }
 }
 
-// One wave per routed row of h (float32 [R, I]); I % 4 == 0.
 __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restrict__ h, int R,
                                                            int I, int8_t* __restrict__ hq,
                                                            float* __restrict__ hs,
@@ -83,22 +127,45 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
   const int p = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (p >= R) return;
   const float* row = h + static_cast<size_t>(p) * I;
+  int8_t* qrow = hq + static_cast<size_t>(p) * I;
+  int8_t* drow = dbg_hq ? dbg_hq + static_cast<size_t>(p) * I : nullptr;
+  const int C = I / 4;   // 16-byte chunks of 4 values
   float amax = 0.0f;
-  for (int c = lane * 4; c < I; c += kWave * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + c);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  if (C <= kRowChunks * kWave) {   // uniform: the row stays in registers
+    float4 v[kRowChunks];
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i)
+      v[i] = *reinterpret_cast<const float4*>(row + min(lane + i * kWave, C - 1) * 4);
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i)
+      if (lane + i * kWave < C) amax = amax_f32x4(v[i], amax);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
+    const float s = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) {
+      const int c = lane + i * kWave;
+      if (c < C) {
+        const uint32_t q = code_f32x4(v[i], s);
+        *reinterpret_cast<uint32_t*>(qrow + c * 4) = q;
+        if (drow) *reinterpret_cast<uint32_t*>(drow + c * 4) = q;
+      }
+    }
+    if (lane == 0) {
+      hs[p] = s;
+      if (dbg_hs) dbg_hs[p] = s;
+    }
+    return;
   }
+  for (int c = lane; c < C; c += kWave)
+    amax = amax_f32x4(*reinterpret_cast<const float4*>(row + c * 4), amax);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
   const float s = amax / 127.0f;
-  for (int c = lane * 4; c < I; c += kWave * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + c);
-    const uint32_t q = static_cast<uint8_t>(quant_code(v.x, s)) |
-                       (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.y, s))) << 8) |
-                       (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.z, s))) << 16) |
-                       (static_cast<uint32_t>(static_cast<uint8_t>(quant_code(v.w, s))) << 24);
-    *reinterpret_cast<uint32_t*>(hq + static_cast<size_t>(p) * I + c) = q;
-    if (dbg_hq) *reinterpret_cast<uint32_t*>(dbg_hq + static_cast<size_t>(p) * I + c) = q;
+  for (int c = lane; c < C; c += kWave) {
+    const uint32_t q = code_f32x4(*reinterpret_cast<const float4*>(row + c * 4), s);
+    *reinterpret_cast<uint32_t*>(qrow + c * 4) = q;
+    if (drow) *reinterpret_cast<uint32_t*>(drow + c * 4) = q;
   }
   if (lane == 0) {
     hs[p] = s;
