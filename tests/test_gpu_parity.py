@@ -373,6 +373,23 @@ CUSTOM_W4A8 = [
 ]
 
 
+def test_int4_gemms_at_the_largest_dim():
+    """H = MOE_MAX_DIM on the MFMA paths with 64-row tiles (the scale strips
+    take the most LDS there): W4A16 and W4A8 against the oracle. I = 512: at
+    this H the bf16 rounding of h alone (W4A16) puts single y elements at
+    1.5% of the row rms (2.1% with I = 128, where y sums only 128 terms)."""
+    wl16 = synth.Workload("w4_maxdim", 312, 64, 16384, 512, 1, 1, "w4a16", "none", 1)
+    x, L = synth.x_bf16(wl16, 0), synth.router_logits(wl16, 0)
+    ref = oracle.moe_layer_w4a16(x, L, 1, expert_getter_w4(wl16, 0))
+    _say("w4a16 max dim")
+    res = run_layer(wl16, x, L, stage_weights(wl16, 0))
+    check_routing_and_perm(res, ref)
+    assert_close(res["y"], ref["y"], "y")
+    assert_close(res["out"], ref["out"], "out")
+    _say("w4a8 max dim")
+    _w4a8_case(wl16.with_(name="w4a8_maxdim", fmt="w4a8"))
+
+
 @pytest.mark.parametrize("case", CUSTOM_W4A8, ids=[c[0] for c in CUSTOM_W4A8])
 def test_w4a8_custom_shapes(case):
     name, wid, T, H, I, E, k = case
