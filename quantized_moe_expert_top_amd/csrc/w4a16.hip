@@ -346,6 +346,7 @@ constexpr int kDecodeMaxR = kDecodeMaxT * 32;
 constexpr int kDecodeBlocks = 512;   // target blocks of the down kernel (2 per CU)
 constexpr int kDecodeGateupBlocks = 512;     // working blocks of the persistent gate/up (2 per CU)
 constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
+constexpr int kSlotThreads = 256;            // threads per slot-per-block gate/up block (512: slower)
 
 // Routing bookkeeping of the fused layer (the last gate/up block): counts,
 // exclusive offsets, active list, stable slot order; writes the routing
@@ -457,8 +458,8 @@ __device__ __forceinline__ void dot_chunk2(const uint4& q0, const uint4& q1, con
 // all of e's rows, later slots with the same expert exit. Where e's rows sit
 // in grouped order follows from wave ballots over the R ids. The last block
 // does the bookkeeping, as in the persistent variant below.
-template <int LK, int NB, int S>
-__global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
+template <int LK, int NB, int S, int NTHR>
+__global__ __launch_bounds__(NTHR) void decode_gateup_slot_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
     int k, int tiles, int* __restrict__ ids_out, float* __restrict__ w_out,
@@ -471,7 +472,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
   int* s_off = reinterpret_cast<int*>(bsum + T * (H / 32));      // [E + 1] (bookkeeping)
   __shared__ int s_ids[kDecodeMaxR];
   __shared__ float s_w[kDecodeMaxR];
-  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR], s_tot[4];
+  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR];
+  __shared__ int s_tot[NTHR / kWave];
   __shared__ int tok[kGemvMaxM];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int R = T * k;
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
   if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
   if (blockIdx.x == gridDim.x - 1) {  // uniform: the bookkeeping block
     __syncthreads();
-    decode_bookkeeping<kThreads>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
+    decode_bookkeeping<NTHR>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
                                  w_out, offsets_out, sorted_out, pos_out, active_out,
                                  n_active_out, rec);
     return;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_slot_kernel(
   }
   if (earlier) return;  // uniform: an earlier slot's block runs expert e
   // s_sorted[m] was written by wave 0, the only wave that reads it (tok fill)
-  gemv_block<0, LK, NB, false>(x, w13, s13, e, tile, p0, M, s_sorted, H, 2 * I, k, T, true, xs,
+  gemv_block<0, LK, NB, false, NTHR>(x, w13, s13, e, tile, p0, M, s_sorted, H, 2 * I, k, T, true, xs,
                                bsum, tok, GemvStore{h, 2 * I});
 }
 
@@ -895,22 +897,22 @@ hipError_t launch_decode_gateup_t(const float* logits, const uint16_t* x, const 
   // slot-per-block while its grid stays within a few blocks per CU (one unit
   // per lane group, all codes in registers); persistent otherwise. Both add
   // the bookkeeping block.
-  constexpr int UB = GemvGeom<0, LK>::UB;
+  constexpr int UB = GemvGeom<0, LK, kSlotThreads>::UB;
   const int tiles = (I + UB - 1) / UB;
   const long long slot_blocks = static_cast<long long>(T) * k * tiles;
   if (NB <= 4 && slot_blocks <= kDecodeSlotMaxBlocks) {
     auto go = [&](auto kern) -> hipError_t {
       const hipError_t e = attr(reinterpret_cast<const void*>(kern));
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slot_blocks) + 1), dim3(kThreads), lds,
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slot_blocks) + 1), dim3(kSlotThreads), lds,
                          s, logits, x, w13, s13, T, H, I, E, k, tiles, ids, w, offsets,
                          sorted_slot, slot_pos, active, n_active, h, rec);
       return hipGetLastError();
     };
     constexpr int NBS = NB <= 4 ? NB : 4;
-    if (E <= 128) return go(&decode_gateup_slot_kernel<LK, NBS, 2>);
-    if (E <= 256) return go(&decode_gateup_slot_kernel<LK, NBS, 4>);
-    return go(&decode_gateup_slot_kernel<LK, NBS, 16>);
+    if (E <= 128) return go(&decode_gateup_slot_kernel<LK, NBS, 2, kSlotThreads>);
+    if (E <= 256) return go(&decode_gateup_slot_kernel<LK, NBS, 4, kSlotThreads>);
+    return go(&decode_gateup_slot_kernel<LK, NBS, 16, kSlotThreads>);
   }
   auto go = [&](auto kern) -> hipError_t {
     const hipError_t e = attr(reinterpret_cast<const void*>(kern));
