@@ -28,6 +28,8 @@
 //    activation rows go through LDS.
 // Gate/up blocks pair gate row n with up row I + n in the same lane and apply
 // SwiGLU in the epilogue (h is stored bf16); down blocks write y (float32).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -119,6 +121,97 @@ __device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int
   }
 }
 
+// One 16-byte chunk (32 codes) of two weight rows against MM staged
+// activation rows (pair-permuted bf16 in LDS; row m starts at xrow[m]): raw dot
+// products, before the bias sum and the scale. Each code dword is widened once
+// (register-held constants: one v_and_or_b32 per pair) and used for all MM
+// rows; per row the dot2 chain runs in the same order whatever MM is, so a
+// row's result does not depend on how many rows share the codes.
+template <int MM>
+__device__ __forceinline__ void dot_chunk_rows(const uint4& q0, const uint4& q1,
+                                               const uint32_t* const (&xrow)[MM], int c,
+                                               const NibbleConsts& nk, float (&d0)[MM],
+                                               float (&d1)[MM]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    uint32_t w0 = (&q0.x)[v], w1 = (&q1.x)[v];
+    asm volatile("" : "+v"(w0), "+v"(w1));
+    uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+    nibble_pairs_r(w0, nk, a0, a1, a2, a3);
+    nibble_pairs_r(w1, nk, b0, b1, b2, b3);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const uint4 xv = reinterpret_cast<const uint4*>(xrow[m] + c * 16)[v];
+      d0[m] = dot2_bf16(a0, xv.x, d0[m]);
+      d0[m] = dot2_bf16(a1, xv.y, d0[m]);
+      d0[m] = dot2_bf16(a2, xv.z, d0[m]);
+      d0[m] = dot2_bf16(a3, xv.w, d0[m]);
+      d1[m] = dot2_bf16(b0, xv.x, d1[m]);
+      d1[m] = dot2_bf16(b1, xv.y, d1[m]);
+      d1[m] = dot2_bf16(b2, xv.z, d1[m]);
+      d1[m] = dot2_bf16(b3, xv.w, d1[m]);
+    }
+  }
+}
+
+// All NB chunks of one lane against MM staged rows (row m at LDS row xr[m]),
+// each chunk's partial sums un-biased and scaled, then summed over the LK
+// lanes of the group: acc0/acc1 (valid in lane lk == 0) are the two output
+// rows' dot products with row m. sc0/sc1 hold each chunk's raw fp16 scale in
+// their low 16 bits.
+template <int MM, int LK, int NB>
+__device__ __forceinline__ void gemv_rows(const uint4 (&q0)[NB], const uint4 (&q1)[NB],
+                                          const uint32_t (&sc0)[NB], const uint32_t (&sc1)[NB],
+                                          const uint32_t* xs, const float* bsum, int rowlen,
+                                          int C, const int (&xr)[MM], int lk,
+                                          const NibbleConsts& nk, float (&acc0)[MM],
+                                          float (&acc1)[MM]) {
+  const uint32_t* xrow[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    xrow[m] = xs + xr[m] * rowlen;
+    acc0[m] = 0.0f;
+    acc1[m] = 0.0f;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int c = lk + b * LK;
+    float d0[MM], d1[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) d0[m] = d1[m] = 0.0f;
+    dot_chunk_rows<MM>(q0[b], q1[b], xrow, c, nk, d0, d1);
+    const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc0[b]));
+    const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc1[b]));
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const float cs = bsum[xr[m] * C + c];
+      acc0[m] += s0 * (d0[m] - cs);
+      acc1[m] += s1 * (d1[m] - cs);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+#pragma unroll
+    for (int sh = LK / 2; sh >= 1; sh >>= 1) {
+      acc0[m] += wave_shfl_xor(acc0[m], sh);
+      acc1[m] += wave_shfl_xor(acc1[m], sh);
+    }
+  }
+}
+
+// Runs f(m0, std::integral_constant<int, MM>{}) over the M rows two at a time
+// (MM = 2, or 1 for an odd last row), so each pass widens the codes once for
+// two rows in straight-line code.
+template <typename F>
+__device__ __forceinline__ void for_row_pairs(int M, F&& f) {
+  for (int m0 = 0; m0 < M; m0 += 2) {
+    if (m0 + 1 < M)
+      f(m0, std::integral_constant<int, 2>{});
+    else
+      f(m0, std::integral_constant<int, 1>{});
+  }
+}
+
 // Per-row result callback: receives the lane-group totals (valid in lane
 // lk == 0) of both rows for grouped row p.
 struct GemvStore {
@@ -187,29 +280,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
   load_batch(0, qa0, qa1, sa);
   if (KIND == 0 && !x_staged) gemv_stage(A, T, K, xs, bsum);
 
-  // one 16-byte chunk (32 codes) of both rows against one staged row
-  auto dot_chunk = [&](const uint4& q0, const uint4& q1, int xr, int c, float& d0, float& d1) {
-    const uint4* xp = reinterpret_cast<const uint4*>(xs + xr * (K / 2) + c * 16);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 xv = xp[v];
-      uint32_t w0 = (&q0.x)[v], w1 = (&q1.x)[v];
-      // keep the widening inside the row loop: hoisting it would hold 4x the
-      // code registers live for every row pass, and most experts see one row
-      asm volatile("" : "+v"(w0), "+v"(w1));
-      uint32_t a0, a1, a2, a3;
-      nibble_pairs(w0, a0, a1, a2, a3);
-      d0 = dot2_bf16(a0, xv.x, d0);
-      d0 = dot2_bf16(a1, xv.y, d0);
-      d0 = dot2_bf16(a2, xv.z, d0);
-      d0 = dot2_bf16(a3, xv.w, d0);
-      nibble_pairs(w1, a0, a1, a2, a3);
-      d1 = dot2_bf16(a0, xv.x, d1);
-      d1 = dot2_bf16(a1, xv.y, d1);
-      d1 = dot2_bf16(a2, xv.z, d1);
-      d1 = dot2_bf16(a3, xv.w, d1);
-    }
-  };
+  const NibbleConsts nk = nibble_consts();
   auto finish = [&](float acc0, float acc1, int m) {
 #pragma unroll
     for (int sh = LK / 2; sh >= 1; sh >>= 1) {
@@ -229,27 +300,36 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
     }
     __syncthreads();
     if (!PIPE) {
-      // all of this lane's codes are in registers: one pass per row
-      for (int m = 0; m < Mc; ++m) {
-        const int xr = (KIND == 0) ? tok[m] : m;
-        float acc0 = 0.0f, acc1 = 0.0f;
+      // all of this lane's codes are in registers: one pass over them for
+      // all rows of the chunk
+      for_row_pairs(Mc, [&](int mb, auto mm) __attribute__((always_inline)) {
+        constexpr int MM = decltype(mm)::value;
+        int xr[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) xr[m] = (KIND == 0) ? tok[mb + m] : mb + m;
+        uint32_t s0a[NB], s1a[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const int c = lk + b * LK;
-          float d0 = 0.0f, d1 = 0.0f;
-          dot_chunk(qa0[b], qa1[b], xr, c, d0, d1);
-          const float cs = bsum[xr * C + c];
-          acc0 += fp16_bits_to_f32(static_cast<uint16_t>(sa[b] & 0xFFFFu)) * (d0 - cs);
-          acc1 += fp16_bits_to_f32(static_cast<uint16_t>(sa[b] >> 16)) * (d1 - cs);
+          s0a[b] = sa[b];
+          s1a[b] = sa[b] >> 16;
         }
-        finish(acc0, acc1, m0 + m);
-      }
+        float acc0[MM], acc1[MM];
+        gemv_rows<MM, LK, NB>(qa0, qa1, s0a, s1a, xs, bsum, K / 2, C, xr, lk, nk, acc0, acc1);
+        if (lk == 0 && valid) {
+#pragma unroll
+          for (int m = 0; m < MM; ++m)
+            st.put<KIND>(static_cast<size_t>(p0 + m0 + mb + m), u, acc0[m], acc1[m]);
+        }
+      });
     } else {
-      // codes stream through two register batches; rows two at a time
+      // codes stream through two register batches; rows two at a time, the
+      // codes widened once for both
       for (int mp = 0; mp < Mc; mp += 2) {
         const bool two = mp + 1 < Mc;
         const int xr0 = (KIND == 0) ? tok[mp] : mp;
         const int xr1 = two ? ((KIND == 0) ? tok[mp + 1] : mp + 1) : xr0;
+        const uint32_t* xrow1[1] = {xs + xr0 * (K / 2)};
+        const uint32_t* xrow2[2] = {xs + xr0 * (K / 2), xs + xr1 * (K / 2)};
         float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
         auto compute_batch = [&](int i0, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
                                  const uint32_t (&sc)[NB]) {
@@ -259,17 +339,20 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
               const int c = lk + (i0 + b) * LK;
               const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu));
               const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16));
-              float d0 = 0.0f, d1 = 0.0f;
-              dot_chunk(q0[b], q1[b], xr0, c, d0, d1);
               const float cs0 = bsum[xr0 * C + c];
-              acc[0][0] += s0 * (d0 - cs0);
-              acc[0][1] += s1 * (d1 - cs0);
               if (two) {
-                float e0 = 0.0f, e1 = 0.0f;
-                dot_chunk(q0[b], q1[b], xr1, c, e0, e1);
+                float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
+                dot_chunk_rows<2>(q0[b], q1[b], xrow2, c, nk, d0, d1);
                 const float cs1 = bsum[xr1 * C + c];
-                acc[1][0] += s0 * (e0 - cs1);
-                acc[1][1] += s1 * (e1 - cs1);
+                acc[0][0] += s0 * (d0[0] - cs0);
+                acc[0][1] += s1 * (d1[0] - cs0);
+                acc[1][0] += s0 * (d0[1] - cs1);
+                acc[1][1] += s1 * (d1[1] - cs1);
+              } else {
+                float d0[1] = {0.0f}, d1[1] = {0.0f};
+                dot_chunk_rows<1>(q0[b], q1[b], xrow1, c, nk, d0, d1);
+                acc[0][0] += s0 * (d0[0] - cs0);
+                acc[0][1] += s1 * (d1[0] - cs0);
               }
             }
           }
@@ -426,31 +509,6 @@ __device__ __forceinline__ void use_regs(const uint4& a, const uint4& b, uint32_
                "v"(b.w), "v"(c), "v"(d));
 }
 
-// One 16-byte chunk (32 codes) of a gate row and its up row against one staged
-// activation row (pair-permuted bf16 in LDS): raw dot products, before the
-// bias sum and the scale.
-__device__ __forceinline__ void dot_chunk2(const uint4& q0, const uint4& q1, const uint32_t* xrow,
-                                           int c, float& d0, float& d1) {
-  const uint4* xp = reinterpret_cast<const uint4*>(xrow + c * 16);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const uint4 xv = xp[v];
-    uint32_t w0 = (&q0.x)[v], w1 = (&q1.x)[v];
-    asm volatile("" : "+v"(w0), "+v"(w1));
-    uint32_t a0, a1, a2, a3;
-    nibble_pairs(w0, a0, a1, a2, a3);
-    d0 = dot2_bf16(a0, xv.x, d0);
-    d0 = dot2_bf16(a1, xv.y, d0);
-    d0 = dot2_bf16(a2, xv.z, d0);
-    d0 = dot2_bf16(a3, xv.w, d0);
-    nibble_pairs(w1, a0, a1, a2, a3);
-    d1 = dot2_bf16(a0, xv.x, d1);
-    d1 = dot2_bf16(a1, xv.y, d1);
-    d1 = dot2_bf16(a2, xv.z, d1);
-    d1 = dot2_bf16(a3, xv.w, d1);
-  }
-}
-
 // Slot-per-block gate/up of the fused decode layer, for small grids: block
 // a * tiles + tile serves routed slot a (token a / k, pick a % k) and one tile
 // of UB units. Its expert e = ids[a] is known right after the top-k, so the
@@ -587,6 +645,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
   const size_t rowb = static_cast<size_t>(H / 2), srow = static_cast<size_t>(H / kGroup);
   const int gid = blockIdx.x * NGB + wv * G + lane / LK, lk = lane % LK;
   const int NGt = nblk * NGB;
+  const NibbleConsts nk = nibble_consts();
   // codes and raw fp16 scales of one unit; the scales stay unpacked so that
   // nothing waits on a load until the unit is computed
   struct Unit {
@@ -612,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       w.s1[b] = S0[I * srow + (c >> 2)];
     }
   };
-  auto run_unit = [&](int q, const Unit& w) {
+  auto run_unit = [&](int q, const Unit& w) __attribute__((always_inline)) {
     // wait for exactly this unit's loads here, in straight-line code, so the
     // row loop below does not drain the other unit's loads as well
 #pragma unroll
@@ -620,25 +679,19 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       use_regs(w.q0[b], w.q1[b], w.s0[b], w.s1[b]);
     const int a = q / I, u = q - a * I;
     const int p0 = s_ap0[a], M = s_am[a];
-    for (int m = 0; m < M; ++m) {
-      const int t = s_atok[a][m];
-      float acc0 = 0.0f, acc1 = 0.0f;
+    for_row_pairs(M, [&](int mb, auto mm) __attribute__((always_inline)) {
+      constexpr int MM = decltype(mm)::value;
+      int xr[MM];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int c = lk + b * LK;
-        float d0 = 0.0f, d1 = 0.0f;
-        dot_chunk2(w.q0[b], w.q1[b], xs + t * (H / 2), c, d0, d1);
-        const float cs = bsum[t * C + c];
-        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(w.s0[b])) * (d0 - cs);
-        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(w.s1[b])) * (d1 - cs);
-      }
+      for (int m = 0; m < MM; ++m) xr[m] = s_atok[a][mb + m];
+      float acc0[MM], acc1[MM];
+      gemv_rows<MM, LK, NB>(w.q0, w.q1, w.s0, w.s1, xs, bsum, H / 2, C, xr, lk, nk, acc0, acc1);
+      if (lk == 0) {
 #pragma unroll
-      for (int sh = LK / 2; sh >= 1; sh >>= 1) {
-        acc0 += wave_shfl_xor(acc0, sh);
-        acc1 += wave_shfl_xor(acc1, sh);
+        for (int m = 0; m < MM; ++m)
+          h[static_cast<size_t>(p0 + mb + m) * I + u] = f32_to_bf16(silu_mul(acc0[m], acc1[m]));
       }
-      if (lk == 0) h[static_cast<size_t>(p0 + m) * I + u] = f32_to_bf16(silu_mul(acc0, acc1));
-    }
+    });
   };
   // units gid, gid + NGt, ...: two register sets alternate
   load_unit(gid, ua);
@@ -741,12 +794,13 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   }
   __syncthreads();
   const int nitems = na * upb;
+  const NibbleConsts nk = nibble_consts();
   auto load_item = [&](int q, Item& w) {
     const int qq = min(q, nitems - 1);
     const int a = qq / upb;
     load_codes(s_e[a], min(u0 + (qq - a * upb), units - 1), w);
   };
-  auto run_item = [&](int q, const Item& w) {
+  auto run_item = [&](int q, const Item& w) __attribute__((always_inline)) {
     // wait for exactly this item's loads here, in straight-line code
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -755,30 +809,23 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     const int uu = q - a * upb;
     const int p0 = s_p0[a], M = s_m[a];
     const bool valid = u0 + uu < units;
-    for (int m = 0; m < M; ++m) {
-      const int xr = p0 + m;
-      float acc0 = 0.0f, acc1 = 0.0f;
+    for_row_pairs(M, [&](int mb, auto mm) __attribute__((always_inline)) {
+      constexpr int MM = decltype(mm)::value;
+      int xr[MM];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int c = lk + b * LK;
-        float d0 = 0.0f, d1 = 0.0f;
-        dot_chunk2(w.q0[b], w.q1[b], xs + xr * (I / 2), c, d0, d1);
-        const float cs = bsum[xr * C + c];
-        acc0 += fp16_bits_to_f32(static_cast<uint16_t>(w.s0[b])) * (d0 - cs);
-        acc1 += fp16_bits_to_f32(static_cast<uint16_t>(w.s1[b])) * (d1 - cs);
-      }
-#pragma unroll
-      for (int sh = LK / 2; sh >= 1; sh >>= 1) {
-        acc0 += wave_shfl_xor(acc0, sh);
-        acc1 += wave_shfl_xor(acc1, sh);
-      }
+      for (int m = 0; m < MM; ++m) xr[m] = p0 + mb + m;
+      float acc0[MM], acc1[MM];
+      gemv_rows<MM, LK, NB>(w.q0, w.q1, w.s0, w.s1, xs, bsum, I / 2, C, xr, lk, nk, acc0, acc1);
       if (lk == 0 && valid) {
-        ybuf[xr * nr + 2 * uu] = acc0;
-        ybuf[xr * nr + 2 * uu + 1] = acc1;
-        *reinterpret_cast<float2*>(y + static_cast<size_t>(xr) * H + 2 * (u0 + uu)) =
-            make_float2(acc0, acc1);
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          ybuf[xr[m] * nr + 2 * uu] = acc0[m];
+          ybuf[xr[m] * nr + 2 * uu + 1] = acc1[m];
+          *reinterpret_cast<float2*>(y + static_cast<size_t>(xr[m]) * H + 2 * (u0 + uu)) =
+              make_float2(acc0[m], acc1[m]);
+        }
       }
-    }
+    });
   };
   // items lg, lg + NG, ...: D register sets rotate so D - 1 items stream
   // while one is computed (the first D are already in flight)
