@@ -69,7 +69,10 @@ struct GemvGeom {
 // Stage activation rows into LDS: 32 values per (row, chunk), pair-permuted,
 // plus each chunk's bias sum 136 * sum(x) taken by the same dot2 chain as the
 // main loop (so all-8 codes cancel to an exact zero). Row m comes from
-// src + m * K.
+// src + m * K. Within a staged row the 16-byte pieces are ordered by
+// (piece v of the chunk, chunk c): lanes that read piece v of consecutive
+// chunks touch consecutive 16-byte slots, so a wave's reads are free of bank
+// conflicts (chunk-major order put lanes 64 bytes apart, four to a bank group).
 // Two (row, chunk) items per thread per pass, both loads issued before use.
 // Thread numbering starts at `first` (rotated), so a caller can keep the
 // staging off waves that are busy with something else.
@@ -97,7 +100,7 @@ __device__ __forceinline__ void gemv_stage_store(int nrows, int K, int i0, const
     if (i >= n) break;
     const int m = i / C, c = i - m * C;
     float bias = 0.0f;
-    uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2) + c * 16);
+    uint4* dst = reinterpret_cast<uint4*>(xs + m * (K / 2)) + c;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const uint4 q = pair_permute(r.v[h][v]);
@@ -105,7 +108,7 @@ __device__ __forceinline__ void gemv_stage_store(int nrows, int K, int i0, const
       bias = dot2_bf16(kBiasPair, q.y, bias);
       bias = dot2_bf16(kBiasPair, q.z, bias);
       bias = dot2_bf16(kBiasPair, q.w, bias);
-      dst[v] = q;
+      dst[v * C] = q;
     }
     bsum[m * C + c] = bias;
   }
@@ -122,14 +125,15 @@ __device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ src, int
 }
 
 // One 16-byte chunk (32 codes) of two weight rows against MM staged
-// activation rows (pair-permuted bf16 in LDS; row m starts at xrow[m]): raw dot
+// activation rows (pair-permuted bf16 in LDS, pieces ordered by (v, chunk); row m
+// starts at xrow[m], C chunks per row): raw dot
 // products, before the bias sum and the scale. Each code dword is widened once
 // (register-held constants: one v_and_or_b32 per pair) and used for all MM
 // rows; per row the dot2 chain runs in the same order whatever MM is, so a
 // row's result does not depend on how many rows share the codes.
 template <int MM>
 __device__ __forceinline__ void dot_chunk_rows(const uint4& q0, const uint4& q1,
-                                               const uint32_t* const (&xrow)[MM], int c,
+                                               const uint32_t* const (&xrow)[MM], int c, int C,
                                                const NibbleConsts& nk, float (&d0)[MM],
                                                float (&d1)[MM]) {
 #pragma unroll
@@ -141,7 +145,7 @@ __device__ __forceinline__ void dot_chunk_rows(const uint4& q0, const uint4& q1,
     nibble_pairs_r(w1, nk, b0, b1, b2, b3);
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-      const uint4 xv = reinterpret_cast<const uint4*>(xrow[m] + c * 16)[v];
+      const uint4 xv = reinterpret_cast<const uint4*>(xrow[m])[v * C + c];
       d0[m] = dot2_bf16(a0, xv.x, d0[m]);
       d0[m] = dot2_bf16(a1, xv.y, d0[m]);
       d0[m] = dot2_bf16(a2, xv.z, d0[m]);
@@ -179,7 +183,7 @@ __device__ __forceinline__ void gemv_rows(const uint4 (&q0)[NB], const uint4 (&q
     float d0[MM], d1[MM];
 #pragma unroll
     for (int m = 0; m < MM; ++m) d0[m] = d1[m] = 0.0f;
-    dot_chunk_rows<MM>(q0[b], q1[b], xrow, c, nk, d0, d1);
+    dot_chunk_rows<MM>(q0[b], q1[b], xrow, c, C, nk, d0, d1);
     const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc0[b]));
     const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc1[b]));
 #pragma unroll
@@ -342,7 +346,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
               const float cs0 = bsum[xr0 * C + c];
               if (two) {
                 float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
-                dot_chunk_rows<2>(q0[b], q1[b], xrow2, c, nk, d0, d1);
+                dot_chunk_rows<2>(q0[b], q1[b], xrow2, c, C, nk, d0, d1);
                 const float cs1 = bsum[xr1 * C + c];
                 acc[0][0] += s0 * (d0[0] - cs0);
                 acc[0][1] += s1 * (d1[0] - cs0);
@@ -350,7 +354,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
                 acc[1][1] += s1 * (d1[1] - cs1);
               } else {
                 float d0[1] = {0.0f}, d1[1] = {0.0f};
-                dot_chunk_rows<1>(q0[b], q1[b], xrow1, c, nk, d0, d1);
+                dot_chunk_rows<1>(q0[b], q1[b], xrow1, c, C, nk, d0, d1);
                 acc[0][0] += s0 * (d0[0] - cs0);
                 acc[0][1] += s1 * (d1[0] - cs0);
               }
