@@ -432,6 +432,7 @@ constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
 constexpr int kDecodeBlocks = 512;   // target blocks of the down kernel (2 per CU)
 constexpr int kDecodeGateupBlocks = 512;     // working blocks of the persistent gate/up (2 per CU)
+constexpr int kDecodeGateupUF1Blocks = 1024;
 constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
 constexpr int kSlotThreads = 256;            // threads per slot-per-block gate/up block (512: slower)
 
@@ -580,8 +581,8 @@ __global__ __launch_bounds__(NTHR) void decode_gateup_slot_kernel(
 // lane group g of the grid takes units g, g + NGt, ... with the codes of two
 // units in flight, so every block streams an equal share whatever na is.
 // LK lanes split the H/32 code chunks of a row, NB = H/32/LK chunks each.
-template <int LK, int NB, int S>
-__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
+template <int LK, int NB, int S, int UF>
+__global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
     int k, int* __restrict__ ids_out, float* __restrict__ w_out, int* __restrict__ offsets_out,
@@ -697,6 +698,15 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       }
     });
   };
+  if (UF == 1) {
+    // units gid, gid + NGt, ...: one unit's codes in flight per lane group;
+    // the other waves of the SIMD cover its load latency
+    for (int q = gid; q < U; q += NGt) {
+      load_unit(q, ua);
+      run_unit(q, ua);
+    }
+    return;
+  }
   // units gid, gid + NGt, ...: two register sets alternate
   load_unit(gid, ua);
   load_unit(gid + NGt, ub);
@@ -710,14 +720,14 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
 
 // NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
 // separate calls). D: work items in flight per lane group.
-template <int LK, int NB, int D>
-__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+template <int LK, int NB, int D, int NTHR>
+__global__ __launch_bounds__(NTHR, NTHR > kThreads ? 2 : 1) void decode_down_kernel(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
     const uint16_t* __restrict__ s2, int T, int H, int I, int E, int k, int upb,
     const int* __restrict__ rec, const int* __restrict__ slot_pos,
     const float* __restrict__ topk_w, float* __restrict__ y, float* __restrict__ out) {
   constexpr int G = kWave / LK;       // lane groups per wave
-  constexpr int NG = 4 * G;           // lane groups per block
+  constexpr int NG = (NTHR / kWave) * G;   // lane groups per block
   extern __shared__ uint32_t lds[];
   const int R = T * k;
   const int C = I / 32;
@@ -781,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) first_codes(lg + d * NG, it[d]);
-  for (int i = tid; i < na; i += kThreads) {
+  for (int i = tid; i < na; i += NTHR) {
     s_e[i] = rec[1 + 3 * i];
     s_p0[i] = rec[2 + 3 * i];
     s_m[i] = rec[3 + 3 * i];
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     s_w[tid] = my_w;
     s_sp[tid] = my_sp;
   }
-  for (int i0 = tid + 2 * kThreads; i0 < n_stage; i0 += 2 * kThreads) {
+  for (int i0 = tid + 2 * NTHR; i0 < n_stage; i0 += 2 * NTHR) {
     StageRegs r;
     gemv_stage_load(h, R, I, i0, r);
     gemv_stage_store(R, I, i0, r, xs, bsum);
@@ -845,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   }
   __syncthreads();
   // combine for this tile's rows, in increasing j
-  for (int idx = tid; idx < T * nr; idx += kThreads) {
+  for (int idx = tid; idx < T * nr; idx += NTHR) {
     const int t = idx / nr, r = idx - t * nr;
     const int n = 2 * u0 + r;
     if (n >= H) continue;
@@ -968,14 +978,14 @@ hipError_t launch_decode_gateup_t(const float* logits, const uint16_t* x, const 
   auto go = [&](auto kern) -> hipError_t {
     const hipError_t e = attr(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(kDecodeGateupBlocks + 1), dim3(kThreads), lds, s, logits, x,
+    hipLaunchKernelGGL(kern, dim3(kDecodeGateupUF1Blocks + 1), dim3(kThreads), lds, s, logits, x,
                        w13, s13, T, H, I, E, k, ids, w, offsets, sorted_slot, slot_pos, active,
                        n_active, h, rec);
     return hipGetLastError();
   };
-  if (E <= 128) return go(&decode_gateup_kernel<LK, NB, 2>);
-  if (E <= 256) return go(&decode_gateup_kernel<LK, NB, 4>);
-  return go(&decode_gateup_kernel<LK, NB, 16>);
+  if (E <= 128) return go(&decode_gateup_kernel<LK, NB, 2, 1>);
+  if (E <= 256) return go(&decode_gateup_kernel<LK, NB, 4, 1>);
+  return go(&decode_gateup_kernel<LK, NB, 16, 1>);
 }
 
 template <int LK, typename... Args>
@@ -1032,19 +1042,19 @@ struct DecodeDownLaunch {
     // tiles that hold many items
     constexpr int NG = 4 * (kWave / LK);
     const int items = (T * k < E ? T * k : E) * upb;
-    auto go = [&](auto kern) -> hipError_t {
+    auto go = [&](auto kern, int nthr) -> hipError_t {
       if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  static_cast<int>(lds));
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, h, w2, s2, T, H, I, E, k,
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(nthr), lds, s, h, w2, s2, T, H, I, E, k,
                          upb, rec, slot_pos, w, y, out);
       return hipGetLastError();
     };
-    if (items > 4 * NG) return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 4>);
-    return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 2>);
+    if (items > 4 * NG) return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 1, 2 * kThreads>, 2 * kThreads);
+    return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 2, kThreads>, kThreads);
   }
 };
 
