@@ -431,8 +431,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
 constexpr int kDecodeBlocks = 512;   // target blocks of the down kernel (2 per CU)
-constexpr int kDecodeGateupBlocks = 512;     // working blocks of the persistent gate/up (2 per CU)
-constexpr int kDecodeGateupUF1Blocks = 1024;
+// Persistent gate/up: 1024 working blocks of 256 threads, four per CU at four
+// waves per SIMD (128 VGPRs). Two units in flight per lane group at two waves
+// per SIMD (85.0 us per step at H 7168 / E 256) and 512-thread blocks (79.4 us)
+// measured slower than this (80.1 us).
+constexpr int kGateupThreads = 256;
+constexpr int kDecodeGateupBlocks = 1024;
 constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
 constexpr int kSlotThreads = 256;            // threads per slot-per-block gate/up block (512: slower)
 
@@ -578,18 +582,18 @@ __global__ __launch_bounds__(NTHR) void decode_gateup_slot_kernel(
 // lists the active experts in order of first pick (expert, grouped offset,
 // rows, their tokens) from the R ids, all waves writing the same table. The
 // work is na * I units (an active expert's gate row u with its up row I + u);
-// lane group g of the grid takes units g, g + NGt, ... with the codes of two
-// units in flight, so every block streams an equal share whatever na is.
+// lane group g of the grid takes units g, g + NGt, ..., so every block streams
+// an equal share whatever na is.
 // LK lanes split the H/32 code chunks of a row, NB = H/32/LK chunks each.
-template <int LK, int NB, int S, int UF>
-__global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kernel(
+template <int LK, int NB, int S, int NTHR>
+__global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ w13, const uint16_t* __restrict__ s13, int T, int H, int I, int E,
     int k, int* __restrict__ ids_out, float* __restrict__ w_out, int* __restrict__ offsets_out,
     int* __restrict__ sorted_out, int* __restrict__ pos_out, int* __restrict__ active_out,
     int* __restrict__ n_active_out, uint16_t* __restrict__ h, int* __restrict__ rec) {
   constexpr int G = kWave / LK;                  // lane groups per wave
-  constexpr int NGB = (kThreads / kWave) * G;    // lane groups per block
+  constexpr int NGB = (NTHR / kWave) * G;        // lane groups per block
   extern __shared__ uint32_t lds[];
   const int C = H / 32;                                          // 16-byte chunks per row
   uint32_t* xs = lds;                                            // [T][H/2]
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kerne
   int* s_off = reinterpret_cast<int*>(bsum + T * C);             // [E + 1] (bookkeeping)
   __shared__ int s_ids[kDecodeMaxR];
   __shared__ float s_w[kDecodeMaxR];
-  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR], s_tot[4];
+  __shared__ int s_sorted[kDecodeMaxR], s_pos[kDecodeMaxR], s_act[kDecodeMaxR], s_tot[NTHR / kWave];
   __shared__ int s_ae[kDecodeMaxR], s_ap0[kDecodeMaxR], s_am[kDecodeMaxR];
   __shared__ int s_atok[kDecodeMaxR][kDecodeMaxT];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kerne
   if (wv < T) wave_topk<S>(logits + static_cast<size_t>(wv) * E, E, k, s_ids + wv * k, s_w + wv * k);
   if (blockIdx.x == nblk) {  // uniform: the bookkeeping block
     __syncthreads();
-    decode_bookkeeping<kThreads>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
+    decode_bookkeeping<NTHR>(s_ids, s_w, s_off, s_sorted, s_pos, s_act, s_tot, R, E, ids_out,
                                  w_out, offsets_out, sorted_out, pos_out, active_out,
                                  n_active_out, rec);
     return;
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kerne
     uint4 q0[NB], q1[NB];
     uint32_t s0[NB], s1[NB];
   };
-  Unit ua, ub;
+  Unit ua;
   auto load_unit = [&](int q, Unit& w) {
     q = min(q, U - 1);
     const int a = q / I, u = q - a * I;
@@ -698,28 +702,20 @@ __global__ __launch_bounds__(kThreads, UF == 1 ? 4 : 2) void decode_gateup_kerne
       }
     });
   };
-  if (UF == 1) {
-    // units gid, gid + NGt, ...: one unit's codes in flight per lane group;
-    // the other waves of the SIMD cover its load latency
-    for (int q = gid; q < U; q += NGt) {
-      load_unit(q, ua);
-      run_unit(q, ua);
-    }
-    return;
-  }
-  // units gid, gid + NGt, ...: two register sets alternate
-  load_unit(gid, ua);
-  load_unit(gid + NGt, ub);
-  for (int q = gid; q < U; q += 2 * NGt) {
+  // units gid, gid + NGt, ...: one unit's codes in flight per lane group; the
+  // other waves of the SIMD (four per SIMD) cover its load latency
+  for (int q = gid; q < U; q += NGt) {
+    load_unit(q, ua);
     run_unit(q, ua);
-    if (q + 2 * NGt < U) load_unit(q + 2 * NGt, ua);
-    if (q + NGt < U) run_unit(q + NGt, ub);
-    if (q + 3 * NGt < U) load_unit(q + 3 * NGt, ub);
   }
 }
 
 // NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
-// separate calls). D: work items in flight per lane group.
+// separate calls). D: work items in flight per lane group. NTHR: block width.
+// Tiles with many items per lane group run 512-thread blocks with one item in
+// flight (two blocks per CU, four waves per SIMD: 99 VGPRs), which measured
+// faster than 256-thread blocks with four items in flight at two waves per
+// SIMD; small tiles keep 256 threads and two items in flight.
 template <int LK, int NB, int D, int NTHR>
 __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 2 : 1) void decode_down_kernel(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
@@ -978,14 +974,14 @@ hipError_t launch_decode_gateup_t(const float* logits, const uint16_t* x, const 
   auto go = [&](auto kern) -> hipError_t {
     const hipError_t e = attr(reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(kDecodeGateupUF1Blocks + 1), dim3(kThreads), lds, s, logits, x,
+    hipLaunchKernelGGL(kern, dim3(kDecodeGateupBlocks + 1), dim3(kGateupThreads), lds, s, logits, x,
                        w13, s13, T, H, I, E, k, ids, w, offsets, sorted_slot, slot_pos, active,
                        n_active, h, rec);
     return hipGetLastError();
   };
-  if (E <= 128) return go(&decode_gateup_kernel<LK, NB, 2, 1>);
-  if (E <= 256) return go(&decode_gateup_kernel<LK, NB, 4, 1>);
-  return go(&decode_gateup_kernel<LK, NB, 16, 1>);
+  if (E <= 128) return go(&decode_gateup_kernel<LK, NB, 2, kGateupThreads>);
+  if (E <= 256) return go(&decode_gateup_kernel<LK, NB, 4, kGateupThreads>);
+  return go(&decode_gateup_kernel<LK, NB, 16, kGateupThreads>);
 }
 
 template <int LK, typename... Args>
