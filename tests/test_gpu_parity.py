@@ -494,6 +494,30 @@ def test_layer_entry_workloads(name, unit):
     np.testing.assert_array_equal(got["out_bits"], again["out_bits"])
 
 
+@pytest.mark.parametrize("case", [("layer_t4_h8192", 308, 4, 8192, 512, 32, 8),
+                                  ("layer_t3_h8192", 308, 3, 8192, 512, 32, 8)],
+                         ids=["t4_h8192", "t3_h8192"])
+def test_layer_entry_wide_tiles(case):
+    """The persistent gate/up (grid past the slot-per-block limit) with an
+    expert that every token picked (3 or 4 rows: two row-pair passes), and the
+    down tiles with more than four items per
+    lane group (512-thread blocks, one item in flight), against the oracle;
+    a second call gives the same bits."""
+    name, wid, T, H, I, E, k = case
+    wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
+    x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+    ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, 0))
+    wts = stage_weights(wl, 0, ref["perm"]["active"])
+    _say("layer entry", name, (T, H, I, E, k))
+    got = _layer_entry(wl, x, L, wts)
+    check_routing_and_perm(got, ref)
+    assert np.diff(ref["perm"]["expert_offsets"]).max() == T   # an expert takes every token
+    assert_close(got["y"], ref["y"], "y")
+    assert_close(got["out"], ref["out"], "out")
+    again = _layer_entry(wl, x, L, wts)
+    np.testing.assert_array_equal(got["out_bits"], again["out_bits"])
+
+
 def test_layer_entry_in_graph_replays():
     """The fused decode layer captured in a HIP graph: every replay matches the
     eager result (the combine counters are cleared inside the layer each time)."""
