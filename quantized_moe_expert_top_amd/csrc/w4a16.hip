@@ -434,8 +434,8 @@ constexpr int kDecodeBlocks = 512;       // target blocks of the 256-thread down
 constexpr int kDecodeWideBlocks = 256;   // target blocks of the 1024-thread down tiles (1 per CU)
 // Persistent gate/up: 1024 working blocks of 256 threads, four per CU at four
 // waves per SIMD (128 VGPRs). Two units in flight per lane group at two waves
-// per SIMD (85.0 us per step at H 7168 / E 256) and 512-thread blocks (79.4 us)
-// measured slower than this (80.1 us).
+// per SIMD (85.0 us per step at H 7168 / E 256), 512-thread blocks (79.4 us)
+// and 1024-thread blocks (72.2 us, against 69.0 us) measured slower.
 constexpr int kGateupThreads = 256;
 constexpr int kDecodeGateupBlocks = 1024;
 constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
