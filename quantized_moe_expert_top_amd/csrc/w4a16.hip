@@ -430,8 +430,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 // atomics cross blocks.
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
-constexpr int kDecodeBlocks = 512;       // target blocks of the 256-thread down tiles (2 per CU)
-constexpr int kDecodeWideBlocks = 256;   // target blocks of the 1024-thread down tiles (1 per CU)
+// Down kernel: 256 blocks of 1024 threads (one per CU, so the staged h rows
+// are read once per CU), one item in flight per lane group at four waves per
+// SIMD. Measured against two 256-thread blocks per CU with two or four items
+// in flight: 27.1 against 37.5 us (decode_large down), 19.55 against 19.81 us
+// per decode_t2 layer.
+constexpr int kDecodeBlocks = 256;
+constexpr int kDecodeThreads = 1024;
 // Persistent gate/up: 1024 working blocks of 256 threads, four per CU at four
 // waves per SIMD (128 VGPRs). Two units in flight per lane group at two waves
 // per SIMD (85.0 us per step at H 7168 / E 256), 512-thread blocks (79.4 us)
@@ -713,10 +718,6 @@ __global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kerne
 
 // NB: code chunks per lane (= K / 32 / LK, at most 4 here; larger K uses the
 // separate calls). D: work items in flight per lane group. NTHR: block width.
-// Tiles with many items per lane group run wide blocks with one item in
-// flight at four waves per SIMD, which measured faster than 256-thread blocks
-// with four items in flight at two waves per SIMD; small tiles keep 256
-// threads and two items in flight.
 template <int LK, int NB, int D, int NTHR>
 __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) void decode_down_kernel(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2,
@@ -1026,26 +1027,13 @@ inline size_t decode_down_lds(int T, int H, int I, int k, int upb) {
   return gemv_lds_bytes(R, I) + static_cast<size_t>(R) * 2 * upb * 4;
 }
 
-// Items per lane group of a 256-thread down tile: (active experts) * upb /
-// lane groups. Tiles with more than four get 1024-thread blocks, one per CU
-// (the staged h rows are read once per CU), with one item in flight per lane
-// group at four waves per SIMD.
-inline bool decode_down_wide(int T, int H, int E, int k, int LK) {
-  const int NG = 4 * (kWave / LK);
-  return (T * k < E ? T * k : E) * decode_down_upb(H, kDecodeBlocks) > 4 * NG;
-}
-inline int decode_down_tile_upb(int T, int H, int E, int k, int LK) {
-  return decode_down_upb(H, decode_down_wide(T, H, E, k, LK) ? kDecodeWideBlocks : kDecodeBlocks);
-}
-
 template <int LK, int NB, bool PIPE>
 struct DecodeDownLaunch {
   static hipError_t run(const uint16_t* h, const uint8_t* w2, const uint16_t* s2, int T, int H,
                         int I, int E, int k, const int* rec, const int* slot_pos, const float* w,
                         float* y, float* out, hipStream_t s) {
     if (PIPE) return hipErrorInvalidValue;  // excluded by the host dispatch rule
-    const bool wide = decode_down_wide(T, H, E, k, LK);
-    const int upb = decode_down_tile_upb(T, H, E, k, LK);
+    const int upb = decode_down_upb(H, kDecodeBlocks);
     const int blocks = (H / 2 + upb - 1) / upb;
     const size_t lds = decode_down_lds(T, H, I, k, upb);
     auto go = [&](auto kern, int nthr) -> hipError_t {
@@ -1059,8 +1047,7 @@ struct DecodeDownLaunch {
                          upb, rec, slot_pos, w, y, out);
       return hipGetLastError();
     };
-    if (wide) return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 1, 4 * kThreads>, 4 * kThreads);
-    return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 2, kThreads>, kThreads);
+    return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 1, kDecodeThreads>, kDecodeThreads);
   }
 };
 
@@ -1400,12 +1387,12 @@ LayerWs layer_carve(void* ws, int T, int I, int E, int k) {
 }
 // The two-kernel decode layer: T <= 4, the down kernel's codes fit one
 // register batch (I / 32 / LK <= 4) and its staged h rows fit LDS.
-bool layer_fused(int T, int H, int I, int E, int k) {
+bool layer_fused(int T, int H, int I, int k) {
   if (T > kDecodeMaxT || T * k > kDecodeMaxR || decode_gateup_lk(H) == 0) return false;
   const int C = I / 32;
   const int LK = (C % 16 == 0 && C >= 64) ? 16 : (C % 8 == 0 ? 8 : 4);
   if (C / LK > 4) return false;
-  return decode_down_lds(T, H, I, k, decode_down_tile_upb(T, H, E, k, LK)) <= 150 * 1024;
+  return decode_down_lds(T, H, I, k, decode_down_upb(H, kDecodeBlocks)) <= 150 * 1024;
 }
 }  // namespace
 
@@ -1422,7 +1409,7 @@ hipError_t launch_w4a16_layer(int T, int H, int I, int E, int k, const float* lo
                               int* offsets, int* sorted_slot, int* slot_pos, int* active,
                               int* n_active, float* y, float* out, void* ws, hipStream_t s) {
   const LayerWs lw = layer_carve(ws, T, I, E, k);
-  if (T > 0 && layer_fused(T, H, I, E, k)) {
+  if (T > 0 && layer_fused(T, H, I, k)) {
     hipError_t err = launch_decode_gateup(logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
                                           sorted_slot, slot_pos, active, n_active, lw.h, lw.rec,
                                           s);
