@@ -112,6 +112,12 @@ __device__ __forceinline__ uint64_t route_key(float l, int e) {
   return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
 }
 
+// The logit a route_key() was built from (-0.0 comes back as +0.0, which it
+// ties with).
+__device__ __forceinline__ float route_key_logit(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 // Wave-wide max / sum through DPP (row_shr 1,2,4,8 inside 16-lane rows, then
 // row_bcast 15/31 across rows) and a read of lane 63: a few cycles per step
 // instead of an LDS permute per step. All 64 lanes must be active.
@@ -166,10 +172,9 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (key[s] == win) key[s] = 0ull;
-    const int e = static_cast<int>(0xFFFFFFFFu - ml);
     if (lane == j) {
-      my_e = e;
-      my_l = row[e];
+      my_e = static_cast<int>(0xFFFFFFFFu - ml);
+      my_l = route_key_logit(mh);   // no reload of the row
     }
   }
   // softmax over the k picks; pick 0 holds the maximum
