@@ -6,11 +6,11 @@
 // batch's rows grouped per expert). Integer work only, so every output is
 // exact and deterministic (integer LDS atomics for the counts, nothing else).
 //
-// Stability inside a round of one slot per thread comes from a wave-level
-// "match": lanes holding the same expert id are found with one ballot per id
-// bit; a lane's rank is the number of matching lanes below it, and per-wave
-// counts kept in LDS order the waves of the block. Up to 8192 slots (E <= 512)
-// one block of 1024 threads does everything in one launch; beyond that,
+// Stability inside a round of 64 slots comes from a wave-level "match": lanes
+// holding the same expert id are found with one ballot per id bit; a lane's
+// rank is the number of matching lanes below it, and per-wave counts kept in
+// LDS order the waves of the block. Up to 8192 slots (E <= 512) one block of
+// 1024 threads does everything in one launch; beyond that,
 // chunks of 1024 slots are handled by one block each, and a block's base per
 // expert is the count of that expert in all earlier chunks (a column prefix
 // sum over the per-chunk histograms).
@@ -172,7 +172,13 @@ __device__ void scatter_keys(const uint32_t (&keys)[MAXR], int R, int E, int nbi
 __device__ __forceinline__ int id_bits(int E) { return 32 - __clz(E); }  // covers 0..E
 
 // Everything in one block of NTHR threads (R <= kChunk with 256 threads, up
-// to kSingleMaxR with 1024): one launch instead of three.
+// to kSingleMaxR with 1024): one launch instead of three. Wave w owns the
+// contiguous slots [w * SPW, (w + 1) * SPW) and walks them in rounds of 64 in
+// increasing order, so a slot's stable position is its expert's offset + the
+// expert's slots in earlier waves + those earlier in its own wave. Each wave
+// keeps its own per-expert counts in LDS (no atomics, no barrier between
+// rounds: a wave's LDS operations complete in order); one pass over the
+// counts turns them into per-wave prefixes.
 template <int NTHR, int MAXR>
 __global__ __launch_bounds__(NTHR) void permute_small_kernel(
     const int* __restrict__ ids, int R, int E, int* __restrict__ offsets,
@@ -182,19 +188,65 @@ __global__ __launch_bounds__(NTHR) void permute_small_kernel(
   extern __shared__ int sm[];
   int* counts = sm;            // [E]
   int* run = counts + E;       // [E]
-  int* wc = run + E;           // [NW * E]
+  int* wc = run + E;           // [NW][E]: per-wave counts, then prefixes over waves
   __shared__ int wave_tot[NW];
-  uint32_t keys[MAXR];         // every slot's id is read from memory once
-  load_keys<NTHR, MAXR>(ids, R, E, 0, keys);
-  for (int i = threadIdx.x; i < (2 + NW) * E; i += NTHR) sm[i] = 0;
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  const int SPW = kWave * ((R + kWave * NW - 1) / (kWave * NW));  // <= 64 * MAXR
+  const int f0 = w * SPW;
+  // every slot's id is read from memory once, all loads in flight together
+  int raw[MAXR];
+  if (R > 0) {   // uniform; with no slot, ids may be NULL
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r)
-    if (keys[r] < static_cast<uint32_t>(E)) atomicAdd(&counts[keys[r]], 1);
+    for (int r = 0; r < MAXR; ++r) raw[r] = ids[min(f0 + r * kWave + lane, R - 1)];
+  }
+  uint32_t keys[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int f = f0 + r * kWave + lane;
+    keys[r] = (R > 0 && r * kWave < SPW && f < R) ? static_cast<uint32_t>(clamp_id(raw[r], E))
+                                                  : static_cast<uint32_t>(E);
+  }
+  for (int i = tid; i < NW * E; i += NTHR) wc[i] = 0;
+  __syncthreads();
+  const int nbits = id_bits(E);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int lp[MAXR];   // position among this wave's slots of the same expert
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    lp[r] = 0;
+    if (r * kWave >= SPW) continue;   // uniform
+    const uint32_t key = keys[r];
+    const uint64_t m = wave_match(key, nbits);
+    const int rank = __popcll(m & below);
+    const bool real = key < static_cast<uint32_t>(E);
+    const int before = real ? wc[w * E + key] : 0;
+    lp[r] = before + rank;
+    if (real && rank == 0) wc[w * E + key] = before + __popcll(m);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NTHR) {
+    int acc = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int c = wc[v * E + e];
+      wc[v * E + e] = acc;
+      acc += c;
+    }
+    counts[e] = acc;
+  }
   __syncthreads();
   offsets_and_active<NTHR>(counts, run, E, R, wave_tot, offsets, active, n_active);
   __syncthreads();
-  scatter_keys<NTHR, MAXR>(keys, R, E, id_bits(E), 0, run, wc, sorted_slot, slot_pos);
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int f = f0 + r * kWave + lane;
+    if (r * kWave < SPW && f < R) {
+      const uint32_t key = keys[r];
+      const int pos = run[key] + wc[w * E + key] + lp[r];
+      sorted_slot[pos] = f;
+      slot_pos[f] = pos;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int* __restrict__ ids,
