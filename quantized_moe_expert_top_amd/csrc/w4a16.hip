@@ -40,6 +40,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGemvMaxT = 4;
 
+// 16-byte load of weight codes that are streamed once per call: the
+// non-temporal hint keeps them from displacing other lines in the caches. With
+// plain loads a decode_large step after a 1 GiB write took 123 us, with this
+// hint 79.5 us (68 us when the memory-side cache holds no other dirty data).
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- GEMV ----
 // KIND 0: gate/up (A = x rows of the tokens, out = h bf16 [R, I]).
 // KIND 1: down    (A = h rows of the expert's block, out = y float32 [R, N]).
@@ -271,8 +281,8 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int i = PIPE ? min(i0 + b, nch - 1) : b;
-      q0[b] = ld16(W0 + i * LK * 16);
-      q1[b] = ld16(W1 + i * LK * 16);
+      q0[b] = ld16_nt(W0 + i * LK * 16);
+      q1[b] = ld16_nt(W1 + i * LK * 16);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -676,8 +686,8 @@ __global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kerne
     const uint16_t* S0 = s13 + r0 * srow;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      w.q0[b] = ld16(W0 + b * LK * 16);
-      w.q1[b] = ld16(W0 + I * rowb + b * LK * 16);
+      w.q0[b] = ld16_nt(W0 + b * LK * 16);
+      w.q1[b] = ld16_nt(W0 + I * rowb + b * LK * 16);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -754,8 +764,8 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
     const uint16_t* S0 = s2 + (static_cast<size_t>(e) * H + 2 * u) * srow;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      w.q0[b] = ld16(W0 + b * LK * 16);
-      w.q1[b] = ld16(W0 + rowb + b * LK * 16);
+      w.q0[b] = ld16_nt(W0 + b * LK * 16);
+      w.q1[b] = ld16_nt(W0 + rowb + b * LK * 16);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -764,7 +774,7 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
       w.s1[b] = S0[srow + (c >> 2)];
     }
   };
-  // The first two items' codes go out before anything else: their expert is
+  // The first D items' codes go out before anything else: their expert is
   // read straight from the record (slot clamped below min(R, E), id clamped to
   // [0, E): every record slot holds a valid expert, the clamps only keep the
   // address in bounds), alongside the count of active experts.
