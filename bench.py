@@ -28,6 +28,9 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK = {"bf16": 2500.0, "int8": 5000.0}   # dense, TFLOP/s (TOP/s for int8)
+# streaming-read ceiling measured on one MI355X with probes/stream_read (plain
+# 16-byte loads, 402.7 MB per kernel): the achievable side of the HBM roofline
+HBM_MEASURED_CEILING_GBS = 6320.0
 METRIC = "MoE-FFN tokens/s; decode HBM GB/s % of peak; prefill MFMA % of peak"
 
 
@@ -309,6 +312,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "frac_of_measured_ceiling": round(achieved / HBM_MEASURED_CEILING_GBS, 4),
         "traffic": tr["bytes_per_launch"] if tr else None,
         "kernel": kernel,
         "avg_launch_us": round(avg_ms * 1e3, 2),
