@@ -499,10 +499,9 @@ def test_layer_entry_workloads(name, unit):
                          ids=["t4_h8192", "t3_h8192"])
 def test_layer_entry_wide_tiles(case):
     """The persistent gate/up (grid past the slot-per-block limit) with an
-    expert that every token picked (3 or 4 rows: two row-pair passes), and the
-    down tiles with more than four items per
-    lane group (512-thread blocks, one item in flight), against the oracle;
-    a second call gives the same bits."""
+    expert that every token picked (3 or 4 rows: two row-pair passes), and
+    down tiles of several items per lane group (H 8192: 16 row pairs per
+    block), against the oracle; a second call gives the same bits."""
     name, wid, T, H, I, E, k = case
     wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
     x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
