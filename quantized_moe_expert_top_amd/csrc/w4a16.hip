@@ -797,8 +797,11 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
     const int e = min(max(rec[1 + 3 * a], 0), E - 1);
     load_codes(e, min(u0 + (q - (q / upb) * upb), units - 1), w);
   };
+  // lane groups past the tile's largest item count (min(R, E) experts) have
+  // nothing to load
 #pragma unroll
-  for (int d = 0; d < D; ++d) first_codes(lg + d * NG, it[d]);
+  for (int d = 0; d < D; ++d)
+    if (lg + d * NG < act * upb) first_codes(lg + d * NG, it[d]);
   for (int i = tid; i < na; i += NTHR) {
     s_e[i] = rec[1 + 3 * i];
     s_p0[i] = rec[2 + 3 * i];
