@@ -440,13 +440,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
 // atomics cross blocks.
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxR = kDecodeMaxT * 32;
-// Down kernel: 256 blocks of 1024 threads (one per CU, so the staged h rows
-// are read once per CU), one item in flight per lane group at four waves per
-// SIMD. Measured against two 256-thread blocks per CU with two or four items
-// in flight: 27.1 against 37.5 us (decode_large down), 19.55 against 19.81 us
-// per decode_t2 layer.
+// Down kernel: 256 blocks (one per CU, so the staged h rows are read once per
+// CU), one item in flight per lane group. 1024 threads (four waves per SIMD),
+// or 512 when a tile's items all fit one lane group each. Measured against
+// two 256-thread blocks per CU with two or four items in flight: 27.1 against
+// 37.5 us (decode_large down), 19.55 against 19.81 us per decode_t2 layer;
+// 512 threads where the items fit: 17.6 against 17.8 us per decode_t2 layer,
+// and 70.3 against 68.6 us per decode_large step where they do not.
 constexpr int kDecodeBlocks = 256;
 constexpr int kDecodeThreads = 1024;
+constexpr int kDecodeSmallThreads = 512;
 // Persistent gate/up: 1024 working blocks of 256 threads, four per CU at four
 // waves per SIMD (128 VGPRs). Two units in flight per lane group at two waves
 // per SIMD (85.0 us per step at H 7168 / E 256), 512-thread blocks (79.4 us)
@@ -1060,6 +1063,10 @@ struct DecodeDownLaunch {
                          upb, rec, slot_pos, w, y, out);
       return hipGetLastError();
     };
+    const int act = T * k < E ? T * k : E;
+    if (act * upb <= (kDecodeSmallThreads / kWave) * (kWave / LK))
+      return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 1, kDecodeSmallThreads>,
+                kDecodeSmallThreads);
     return go(&decode_down_kernel<LK, (NB < 1 ? 1 : NB), 1, kDecodeThreads>, kDecodeThreads);
   }
 };
