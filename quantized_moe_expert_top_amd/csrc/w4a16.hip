@@ -456,7 +456,7 @@ constexpr int kDecodeSmallThreads = 512;
 // and 1024-thread blocks (72.2 us, against 69.0 us) measured slower.
 constexpr int kGateupThreads = 256;
 constexpr int kDecodeGateupBlocks = 1024;
-constexpr int kDecodeSlotMaxBlocks = 1024;   // largest grid of the slot-per-block gate/up
+constexpr int kDecodeSlotMaxBlocks = 2048;   // largest grid of the slot-per-block gate/up
 constexpr int kSlotThreads = 256;            // threads per slot-per-block gate/up block (512: slower)
 
 // Routing bookkeeping of the fused layer (the last gate/up block): counts,
@@ -946,14 +946,22 @@ hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                                     N, topk, max_active, T, s);
 }
 
-// Lane split of the fused gate/up: the smallest LK in {8, 16, 32} dividing the
-// H/32 code chunks of a row with at most 4 chunks per lane, else at most 8;
-// 0 if none.
+// Lane split of the fused gate/up: an LK in {8, 16, 32} dividing the H/32
+// code chunks of a row with at most 4 chunks per lane, else at most 8; 0 if
+// none. Rows of 64 or more chunks take the largest such LK (shorter dot
+// chains per lane: 17.6 -> 17.2 us per decode_t2 layer, same-box A/B),
+// shorter rows the smallest (the lane split of the stand-alone GEMV there).
 inline int decode_gateup_lk(int H) {
   const int C = H / 32;
-  for (int cap = 4; cap <= 8; cap *= 2)
-    for (int lk = 8; lk <= 32; lk *= 2)
-      if (C % lk == 0 && C / lk <= cap) return lk;
+  for (int cap = 4; cap <= 8; cap *= 2) {
+    if (C >= 64) {
+      for (int lk = 32; lk >= 8; lk /= 2)
+        if (C % lk == 0 && C / lk <= cap) return lk;
+    } else {
+      for (int lk = 8; lk <= 32; lk *= 2)
+        if (C % lk == 0 && C / lk <= cap) return lk;
+    }
+  }
   return 0;
 }
 
