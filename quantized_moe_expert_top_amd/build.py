@@ -65,14 +65,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    probe = os.path.join(HERE, "probes", "stream_read")
-    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature",
-                        "-Xclang", "-packed-fp32-ops", probe + ".hip", "-o", probe],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
+    probes = [os.path.join(HERE, "probes", name) for name in ("stream_read", "mfma_peak")]
+    for probe in probes:
+        r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature",
+                            "-Xclang", "-packed-fp32-ops", probe + ".hip", "-o", probe],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
     if verbose:
-        print(f"built {LIB} and {probe}")
+        print(f"built {LIB} and {', '.join(probes)}")
     return LIB
 
 
