@@ -495,13 +495,16 @@ def test_layer_entry_workloads(name, unit):
 
 
 @pytest.mark.parametrize("case", [("layer_t4_h8192", 308, 4, 8192, 512, 32, 8),
-                                  ("layer_t3_h8192", 308, 3, 8192, 512, 32, 8)],
-                         ids=["t4_h8192", "t3_h8192"])
+                                  ("layer_t3_h8192", 308, 3, 8192, 512, 32, 8),
+                                  ("layer_t4_h2048_k4", 328, 4, 2048, 768, 16, 4)],
+                         ids=["t4_h8192", "t3_h8192", "t4_h2048_k4"])
 def test_layer_entry_wide_tiles(case):
-    """The persistent gate/up (grid past the slot-per-block limit) with an
-    expert that every token picked (3 or 4 rows: two row-pair passes), and
-    down tiles of several items per lane group (H 8192: 16 row pairs per
-    block), against the oracle; a second call gives the same bits."""
+    """Fused layers with an expert that every token picked (3 or 4 rows: two
+    row-pair passes), against the oracle; a second call gives the same bits.
+    H 8192: the persistent gate/up (grid past the slot-per-block limit) and
+    down tiles of several items per lane group (16 row pairs per block).
+    H 2048, 16 routed slots: the slot-per-block gate/up with 32 lanes per
+    unit."""
     name, wid, T, H, I, E, k = case
     wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
     x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
