@@ -781,7 +781,14 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
   // read straight from the record (slot clamped below min(R, E), id clamped to
   // [0, E): every record slot holds a valid expert, the clamps only keep the
   // address in bounds), alongside the count of active experts.
-  // the first pass of h rows goes out first: it depends on nothing
+  // the record's expert ids go out first: loads complete in issue order, so
+  // the codes that depend on them wait for nothing else; the first pass of h
+  // rows follows (it depends on nothing)
+  const int act = R < E ? R : E;
+  int rec_e[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) rec_e[d] = rec[1 + 3 * min((lg + d * NG) / upb, act - 1)];
+  const int na = rec[0];
   const int n_stage = R * C;
   StageRegs h0;
   gemv_stage_load(h, R, I, tid, h0);
@@ -793,18 +800,14 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
     my_w = topk_w[tid];
     my_sp = slot_pos[tid];
   }
-  const int act = R < E ? R : E;
-  const int na = rec[0];
-  auto first_codes = [&](int q, Item& w) {
-    const int a = min(q / upb, act - 1);
-    const int e = min(max(rec[1 + 3 * a], 0), E - 1);
-    load_codes(e, min(u0 + (q - (q / upb) * upb), units - 1), w);
-  };
   // lane groups past the tile's largest item count (min(R, E) experts) have
   // nothing to load
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (lg + d * NG < act * upb) first_codes(lg + d * NG, it[d]);
+  for (int d = 0; d < D; ++d) {
+    const int q = lg + d * NG;
+    if (q < act * upb)
+      load_codes(min(max(rec_e[d], 0), E - 1), min(u0 + (q - (q / upb) * upb), units - 1), it[d]);
+  }
   for (int i = tid; i < na; i += NTHR) {
     s_e[i] = rec[1 + 3 * i];
     s_p0[i] = rec[2 + 3 * i];
