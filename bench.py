@@ -304,7 +304,7 @@ def main():
     flops_per_call = 6.0 * wl.H * wl.I * wl.T * wl.k
     # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
     # a copy of known size), valid only for the kernel sources they were taken on
-    from quantized_moe_expert_top_amd import traffic as traffic_store
+    import traffic as traffic_store
     tr = traffic_store.lookup(wl.name)
     roofline = {
         "bound": "hbm",

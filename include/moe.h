@@ -8,11 +8,12 @@
  * grouped down projection, and a weighted combine of each token's k expert
  * outputs. Sources of each step are cited at its entry point:
  *   [PV-fast]   page "Performance and verification", section "Why it is fast"
- *               (every routed expert a prompt batch calls is read once for the
- *               whole batch; grouped dispatches instead of per-matrix ones; dot
- *               products on quantized weights as stored; routed experts of a
- *               prompt as grouped int8 tensor-core GEMMs; one graph per decode
- *               step with no host synchronization inside).
+ *               (each active expert's weights are streamed once per call for
+ *               all of the rows routed to it; one grouped launch covers all
+ *               experts; the quantized weights enter the dot products as
+ *               stored; prompt-sized batches of routed experts run as grouped
+ *               int8 tensor-core GEMMs; a decode step is one graph with no
+ *               host synchronization inside).
  *   [PV-verify] same page, section "How it is verified" (router ids and other
  *               integer outputs exact; floats within rounding bands).
  *   [MR]        page "Measured results" (header: W4A16 g128 weights; "Speed":
@@ -22,6 +23,7 @@
  *               drains the GPU pipeline; here nothing syncs inside a layer).
  *
  * Conventions (all entry points):
+ *   - Every call returns a moe_status; MOE_OK means the work was enqueued.
  *   - Tensor pointers are DEVICE pointers to row-major contiguous arrays,
  *     16-byte aligned. bf16 and fp16 travel as uint16_t bit patterns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -74,7 +76,7 @@ typedef enum {
 } moe_status;
 
 /* Static string for a status code. */
-MOE_API const char* moe_status_str(int status);
+MOE_API const char* moe_status_str(moe_status status);
 /* Detail of the last non-OK status returned on this thread ("" if none). */
 MOE_API const char* moe_last_error(void);
 MOE_API int moe_abi_version(void);
@@ -90,7 +92,7 @@ MOE_API int moe_abi_version(void);
  *   logits   float32 [T, E]  (output; feeds moe_route_topk or moe_layer_w4a16)
  * Requires H % 64 == 0, 1 <= E <= MOE_MAX_EXPERTS, T >= 0.
  */
-MOE_API int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T,
+MOE_API moe_status moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T,
                       int32_t H, int32_t E, float* logits, void* stream);
 
 /*
@@ -103,7 +105,7 @@ MOE_API int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32
  *   topk_w   float32 [T, k]  (output)
  * Requires 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK), T >= 0.
  */
-MOE_API int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+MOE_API moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                    int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
@@ -123,7 +125,7 @@ MOE_API int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  * Ids must lie in [0, E).
  */
 MOE_API size_t moe_permute_workspace(int32_t T, int32_t E, int32_t k);
-MOE_API int moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+MOE_API moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
                 int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_pos,
                 int32_t* active, int32_t* n_active,
                 void* ws, size_t ws_bytes, void* stream);
@@ -160,7 +162,7 @@ typedef struct {
  * GEMV; larger T a bf16 MFMA grouped GEMM; both meet the same tolerance.
  */
 MOE_API size_t moe_w4a16_workspace(const moe_shape* shape);
-MOE_API int moe_grouped_w4a16_ffn(const moe_shape* shape, const uint16_t* x,
+MOE_API moe_status moe_grouped_w4a16_ffn(const moe_shape* shape, const uint16_t* x,
                           const uint8_t* w13, const uint16_t* s13,
                           const uint8_t* w2, const uint16_t* s2,
                           const int32_t* expert_offsets, const int32_t* sorted_slot,
@@ -175,18 +177,21 @@ MOE_API int moe_grouped_w4a16_ffn(const moe_shape* shape, const uint16_t* x,
  * per decode step, no host synchronization inside) [MS] (no per-layer host
  * probe)
  * For T <= 4 (decode) it runs two kernels instead of the five launches of the
- * separate calls: every block of the first routes all T tokens itself,
- * rebuilds the permutation in LDS and runs its gate/up tile (block 0 writes
- * the routing outputs); the second runs the down tiles and the combine, whose
- * k-ordered sum for a (token, row tile) is taken by whichever block completes
- * that token's k rows last (an integer counter decides; the order of the sum
- * is fixed, so results are bitwise those of moe_combine's order).
+ * separate calls. In the first, every block routes all T tokens itself, finds
+ * which rows of the grouped order its expert owns, and runs its gate/up units,
+ * writing h; one extra block, the last of the grid, does no GEMV work and
+ * writes the routing outputs, the permutation and a per-expert record for the
+ * second kernel. In the second, each block owns a tile of output rows of H for
+ * every active expert: it stages all routed h rows in LDS, keeps every expert
+ * output of its tile there, and takes the combine for its rows inside the
+ * block, summing the k picks in increasing j (the order of moe_combine). No
+ * counters, atomics or fences cross blocks.
  * For larger T it enqueues the four steps. `logits` float32 [T, E]; other
  * arguments as in the individual calls. Requires H % 128 == 0, I % 128 == 0.
  * `ws` must hold moe_layer_w4a16_workspace(shape) bytes.
  */
 MOE_API size_t moe_layer_w4a16_workspace(const moe_shape* shape);
-MOE_API int moe_layer_w4a16(const moe_shape* shape, const float* logits, const uint16_t* x,
+MOE_API moe_status moe_layer_w4a16(const moe_shape* shape, const float* logits, const uint16_t* x,
                             const uint8_t* w13, const uint16_t* s13,
                             const uint8_t* w2, const uint16_t* s2,
                             int32_t* topk_ids, float* topk_w,
@@ -222,7 +227,7 @@ typedef struct {
  * receive the intermediates. `ws` must hold moe_w8a8_workspace(shape) bytes.
  */
 MOE_API size_t moe_w8a8_workspace(const moe_shape* shape);
-MOE_API int moe_grouped_w8a8_ffn(const moe_shape* shape, const uint16_t* x,
+MOE_API moe_status moe_grouped_w8a8_ffn(const moe_shape* shape, const uint16_t* x,
                          const int8_t* w13, const float* s13,
                          const int8_t* w2, const float* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
@@ -254,7 +259,7 @@ typedef struct {
  * moe_w4a8_workspace(shape) bytes.
  */
 MOE_API size_t moe_w4a8_workspace(const moe_shape* shape);
-MOE_API int moe_grouped_w4a8_ffn(const moe_shape* shape, const uint16_t* x,
+MOE_API moe_status moe_grouped_w4a8_ffn(const moe_shape* shape, const uint16_t* x,
                          const uint8_t* w13, const uint16_t* s13,
                          const uint8_t* w2, const uint16_t* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
@@ -263,14 +268,18 @@ MOE_API int moe_grouped_w4a8_ffn(const moe_shape* shape, const uint16_t* x,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_combine — weighted sum of each token's k expert outputs.
- * out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[slot_pos[t*k + j], :],
- * accumulated in float32 in increasing j (fixed order, no atomics).
+ * moe_combine — weighted sum of each token's k expert outputs. [PV-verify]
+ * (floats within rounding bands of an f64 reference; results reproducible)
+ * The pages print no formula for this step; this call takes its plainest
+ * reading: a token's output is the sum of its k expert outputs weighted by
+ * its router weights, in pick order j (the order moe_route_topk writes),
+ * accumulated in float32 with no atomics, so two runs give the same bits:
+ * out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[slot_pos[t*k + j], :].
  *   y float32 [T*k, H] (grouped order), slot_pos int32 [T*k],
  *   topk_w float32 [T, k], out float32 [T, H].
  * Requires H % 8 == 0.
  */
-MOE_API int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w,
+MOE_API moe_status moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w,
                 int32_t T, int32_t H, int32_t k, float* out, void* stream);
 
 /*
@@ -286,7 +295,7 @@ MOE_API int moe_combine(const float* y, const int32_t* slot_pos, const float* to
  * Requires L >= 0, 1 <= E <= MOE_MAX_EXPERTS, offsets_stride >= E + 1.
  * Calls that update the same counts must be ordered (one stream).
  */
-MOE_API int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
+MOE_API moe_status moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
                                  int32_t L, int32_t E, uint64_t* counts, void* stream);
 
 /*
@@ -297,7 +306,7 @@ MOE_API int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t 
  *   hot_ids int32  [L, n] (output)
  * Requires L >= 0, 1 <= E <= MOE_MAX_EXPERTS, 0 <= n <= E.
  */
-MOE_API int moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n,
+MOE_API moe_status moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n,
                         int32_t* hot_ids, void* stream);
 
 #ifdef __cplusplus

@@ -15,7 +15,7 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
-int fail(int status, const char* fmt, ...) {
+moe_status fail(moe_status status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
@@ -29,7 +29,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
-int check_device() {
+moe_status check_device() {
   int dev = -1;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess)
@@ -51,12 +51,12 @@ int check_device() {
   return MOE_OK;
 }
 
-int launched(hipError_t err, const char* what) {
+moe_status launched(hipError_t err, const char* what) {
   if (err != hipSuccess) return fail(MOE_EDEVICE, "%s: %s", what, hipGetErrorString(err));
   return MOE_OK;
 }
 
-int check_route_dims(int32_t T, int32_t E, int32_t k) {
+moe_status check_route_dims(int32_t T, int32_t E, int32_t k) {
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
   if (k < 1 || k > E || k > MOE_MAX_TOPK)
@@ -66,9 +66,9 @@ int check_route_dims(int32_t T, int32_t E, int32_t k) {
   return MOE_OK;
 }
 
-int check_shape(const moe_shape* s, int hmod, int imod) {
+moe_status check_shape(const moe_shape* s, int hmod, int imod) {
   if (!s) return fail(MOE_EINVAL, "shape is NULL");
-  int st = check_route_dims(s->T, s->E, s->k);
+  moe_status st = check_route_dims(s->T, s->E, s->k);
   if (st) return st;
   if (s->H < hmod || s->H % hmod) return fail(MOE_ESHAPE, "H = %d must be a positive multiple of %d", s->H, hmod);
   if (s->I < imod || s->I % imod) return fail(MOE_ESHAPE, "I = %d must be a positive multiple of %d", s->I, imod);
@@ -94,7 +94,7 @@ int check_shape(const moe_shape* s, int hmod, int imod) {
 
 extern "C" {
 
-const char* moe_status_str(int s) {
+const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
@@ -111,7 +111,7 @@ const char* moe_last_error(void) { return g_last_error; }
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
+moe_status moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
                       int32_t E, float* logits, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
@@ -122,22 +122,22 @@ int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T, in
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_router);
   REQUIRE_PTR(logits);
-  int st;
-  if ((st = check_device())) return st;
+  moe_status st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_router_logits(x, w_router, T, H, E, logits,
                                             static_cast<hipStream_t>(stream)),
                   "moe_router_logits launch");
 }
 
-int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
                    float* topk_w, void* stream) {
-  int st = check_route_dims(T, E, k);
+  moe_status st = check_route_dims(T, E, k);
   if (st) return st;
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(logits);
   REQUIRE_PTR(topk_ids);
   REQUIRE_PTR(topk_w);
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w,
                                          static_cast<hipStream_t>(stream)),
                   "moe_route_topk launch");
@@ -148,10 +148,10 @@ size_t moe_permute_workspace(int32_t T, int32_t E, int32_t k) {
   return moe::permute_workspace_bytes(T, E, k);
 }
 
-int moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
                 int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_pos,
                 int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_route_dims(T, E, k);
+  moe_status st = check_route_dims(T, E, k);
   if (st) return st;
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(n_active);
@@ -167,7 +167,7 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
       return fail(MOE_EWORKSPACE, "permute workspace %zu < %zu bytes", ws_bytes, need);
     REQUIRE_PTR(ws);
   }
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_permute(topk_ids, T, E, k, expert_offsets, sorted_slot, slot_pos,
                                       active, n_active, ws, static_cast<hipStream_t>(stream)),
                   "moe_permute launch");
@@ -178,12 +178,12 @@ size_t moe_w4a16_workspace(const moe_shape* s) {
   return moe::w4a16_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
 }
 
-int moe_grouped_w4a16_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
+moe_status moe_grouped_w4a16_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
                           const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
                           const int32_t* expert_offsets, const int32_t* sorted_slot,
                           const int32_t* active, const int32_t* n_active, float* y, void* ws,
                           size_t ws_bytes, void* stream) {
-  int st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  moe_status st = check_shape(s, MOE_GROUP, MOE_GROUP);
   if (st) return st;
   if (s->T == 0) return MOE_OK;
   REQUIRE_PTR(x);
@@ -199,7 +199,7 @@ int moe_grouped_w4a16_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* 
   const size_t need = moe::w4a16_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "w4a16 workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE_PTR(ws);
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_w4a16_ffn(s->T, s->H, s->I, s->E, s->k, x, w13, s13, w2, s2,
                                         expert_offsets, sorted_slot, active, n_active, y, ws,
                                         static_cast<hipStream_t>(stream)),
@@ -211,13 +211,13 @@ size_t moe_layer_w4a16_workspace(const moe_shape* s) {
   return moe::w4a16_layer_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
 }
 
-int moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16_t* x,
+moe_status moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16_t* x,
                     const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
                     const uint16_t* s2, int32_t* topk_ids, float* topk_w,
                     int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_pos,
                     int32_t* active, int32_t* n_active, float* y, float* out, void* ws,
                     size_t ws_bytes, void* stream) {
-  int st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  moe_status st = check_shape(s, MOE_GROUP, MOE_GROUP);
   if (st) return st;
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(n_active);
@@ -239,7 +239,7 @@ int moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16_t* x,
     REQUIRE_PTR(y);
     REQUIRE_PTR(out);
   }
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_w4a16_layer(s->T, s->H, s->I, s->E, s->k, logits, x, w13, s13, w2,
                                           s2, topk_ids, topk_w, expert_offsets, sorted_slot,
                                           slot_pos, active, n_active, y, out, ws,
@@ -252,12 +252,12 @@ size_t moe_w4a8_workspace(const moe_shape* s) {
   return moe::w4a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
 }
 
-int moe_grouped_w4a8_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
+moe_status moe_grouped_w4a8_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w13,
                          const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
                          const int32_t* active, const int32_t* n_active, float* y,
                          const moe_w4a8_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  moe_status st = check_shape(s, MOE_GROUP, MOE_GROUP);
   if (st) return st;
   if (s->T == 0) return MOE_OK;
   REQUIRE_PTR(x);
@@ -280,7 +280,7 @@ int moe_grouped_w4a8_ffn(const moe_shape* s, const uint16_t* x, const uint8_t* w
   const size_t need = moe::w4a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "w4a8 workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE_PTR(ws);
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_w4a8_ffn(s->T, s->H, s->I, s->E, s->k, x, w13, s13, w2, s2,
                                        expert_offsets, sorted_slot, y, d, ws,
                                        static_cast<hipStream_t>(stream)),
@@ -292,12 +292,12 @@ size_t moe_w8a8_workspace(const moe_shape* s) {
   return moe::w8a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
 }
 
-int moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int8_t* w13,
+moe_status moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int8_t* w13,
                          const float* s13, const int8_t* w2, const float* s2,
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
                          const int32_t* active, const int32_t* n_active, float* y,
                          const moe_w8a8_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_shape(s, 64, 64);
+  moe_status st = check_shape(s, 64, 64);
   if (st) return st;
   if (s->T == 0) return MOE_OK;
   REQUIRE_PTR(x);
@@ -320,14 +320,14 @@ int moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int8_t* w1
   const size_t need = moe::w8a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "w8a8 workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE_PTR(ws);
-  if ((st = check_device())) return st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_w8a8_ffn(s->T, s->H, s->I, s->E, s->k, x, w13, s13, w2, s2,
                                        expert_offsets, sorted_slot, active, n_active, y, d, ws,
                                        static_cast<hipStream_t>(stream)),
                   "moe_grouped_w8a8_ffn launch");
 }
 
-int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w, int32_t T,
+moe_status moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w, int32_t T,
                 int32_t H, int32_t k, float* out, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_ESHAPE, "k = %d outside [1, %d]", k, MOE_MAX_TOPK);
@@ -339,14 +339,14 @@ int moe_combine(const float* y, const int32_t* slot_pos, const float* topk_w, in
   REQUIRE_PTR(slot_pos);
   REQUIRE_PTR(topk_w);
   REQUIRE_PTR(out);
-  int st = check_device();
+  moe_status st = check_device();
   if (st) return st;
   return launched(moe::launch_combine(y, slot_pos, topk_w, T, H, k, out,
                                       static_cast<hipStream_t>(stream)),
                   "moe_combine launch");
 }
 
-int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
+moe_status moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_stride,
                                  int32_t L, int32_t E, uint64_t* counts, void* stream) {
   if (L < 0) return fail(MOE_EINVAL, "L = %d < 0", L);
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
@@ -355,15 +355,15 @@ int moe_expert_counts_accumulate(const int32_t* expert_offsets, int64_t offsets_
   if (L == 0) return MOE_OK;
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(counts);
-  int st;
-  if ((st = check_device())) return st;
+  moe_status st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_expert_counts(expert_offsets, offsets_stride, L, E,
                                             reinterpret_cast<unsigned long long*>(counts),
                                             static_cast<hipStream_t>(stream)),
                   "moe_expert_counts_accumulate launch");
 }
 
-int moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n, int32_t* hot_ids,
+moe_status moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n, int32_t* hot_ids,
                         void* stream) {
   if (L < 0) return fail(MOE_EINVAL, "L = %d < 0", L);
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ESHAPE, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
@@ -371,8 +371,8 @@ int moe_expert_hot_rank(const uint64_t* counts, int32_t L, int32_t E, int32_t n,
   if (L == 0 || n == 0) return MOE_OK;
   REQUIRE_PTR(counts);
   REQUIRE_PTR(hot_ids);
-  int st;
-  if ((st = check_device())) return st;
+  moe_status st;
+  if ((st = check_device()) != MOE_OK) return st;
   return launched(moe::launch_hot_rank(reinterpret_cast<const unsigned long long*>(counts), L, E, n,
                                        hot_ids, static_cast<hipStream_t>(stream)),
                   "moe_expert_hot_rank launch");

@@ -674,11 +674,13 @@ __global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kerne
   const int gid = blockIdx.x * NGB + wv * G + lane / LK, lk = lane % LK;
   const int NGt = nblk * NGB;
   const NibbleConsts nk = nibble_consts();
-  // codes and raw fp16 scales of one unit; the scales stay unpacked so that
-  // nothing waits on a load until the unit is computed
+  // codes and raw fp16 scales of one unit (a chunk's gate and up scales
+  // share one register: the low half the gate row's, the high half the up
+  // row's); the scales stay unconverted so that nothing waits on a load until
+  // the unit is computed
   struct Unit {
     uint4 q0[NB], q1[NB];
-    uint32_t s0[NB], s1[NB];
+    uint32_t sc[NB];
   };
   Unit ua;
   auto load_unit = [&](int q, Unit& w) {
@@ -692,28 +694,36 @@ __global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kerne
       w.q0[b] = ld16_nt(W0 + b * LK * 16);
       w.q1[b] = ld16_nt(W0 + I * rowb + b * LK * 16);
     }
+    // chunk c = lk + b * LK has scale group c / 4 = lk / 4 + b * LK / 4: one
+    // base address per row and compile-time offsets
+    const uint16_t* Sg = S0 + (lk >> 2);
+    const uint16_t* Su = Sg + I * srow;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int c = lk + b * LK;
-      w.s0[b] = S0[c >> 2];
-      w.s1[b] = S0[I * srow + (c >> 2)];
-    }
+    for (int b = 0; b < NB; ++b)
+      w.sc[b] = static_cast<uint32_t>(Sg[b * (LK / 4)]) |
+                (static_cast<uint32_t>(Su[b * (LK / 4)]) << 16);
   };
   auto run_unit = [&](int q, const Unit& w) __attribute__((always_inline)) {
     // wait for exactly this unit's loads here, in straight-line code, so the
     // row loop below does not drain the other unit's loads as well
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      use_regs(w.q0[b], w.q1[b], w.s0[b], w.s1[b]);
+      use_regs(w.q0[b], w.q1[b], w.sc[b], w.sc[b]);
     const int a = q / I, u = q - a * I;
     const int p0 = s_ap0[a], M = s_am[a];
+    uint32_t s0[NB], s1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      s0[b] = w.sc[b];
+      s1[b] = w.sc[b] >> 16;
+    }
     for_row_pairs(M, [&](int mb, auto mm) __attribute__((always_inline)) {
       constexpr int MM = decltype(mm)::value;
       int xr[MM];
 #pragma unroll
       for (int m = 0; m < MM; ++m) xr[m] = s_atok[a][mb + m];
       float acc0[MM], acc1[MM];
-      gemv_rows<MM, LK, NB>(w.q0, w.q1, w.s0, w.s1, xs, bsum, H / 2, C, xr, lk, nk, acc0, acc1);
+      gemv_rows<MM, LK, NB>(w.q0, w.q1, s0, s1, xs, bsum, H / 2, C, xr, lk, nk, acc0, acc1);
       if (lk == 0) {
 #pragma unroll
         for (int m = 0; m < MM; ++m)
@@ -770,11 +780,12 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
       w.q0[b] = ld16_nt(W0 + b * LK * 16);
       w.q1[b] = ld16_nt(W0 + rowb + b * LK * 16);
     }
+    // chunk c = lk + b * LK has scale group lk / 4 + b * LK / 4
+    const uint16_t* Sg = S0 + (lk >> 2);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int c = lk + b * LK;
-      w.s0[b] = S0[c >> 2];
-      w.s1[b] = S0[srow + (c >> 2)];
+      w.s0[b] = Sg[b * (LK / 4)];
+      w.s1[b] = Sg[srow + b * (LK / 4)];
     }
   };
   // The first D items' codes go out before anything else: their expert is
@@ -950,13 +961,17 @@ hipError_t launch_gemv(const uint16_t* A, const uint8_t* W, const uint16_t* S,
 }
 
 // Lane split of the fused gate/up: an LK in {8, 16, 32} dividing the H/32
-// code chunks of a row with at most 4 chunks per lane, else at most 8; 0 if
-// none. Rows of 64 or more chunks take the largest such LK (shorter dot
-// chains per lane: 17.6 -> 17.2 us per decode_t2 layer, same-box A/B),
-// shorter rows the smallest (the lane split of the stand-alone GEMV there).
+// code chunks of a row with at most 4 chunks per lane, else (rows of 256 or
+// more chunks) a whole wave per unit with at most 4 chunks per lane, else at
+// most 7 (eight chunks of two rows, with their scales, need more than the
+// 128 registers of four waves per SIMD); 0 if none. Rows of 64 or more chunks
+// take the largest such LK (shorter dot chains per lane: 17.6 -> 17.2 us per
+// decode_t2 layer, same-box A/B), shorter rows the smallest (the lane split
+// of the stand-alone GEMV there).
 inline int decode_gateup_lk(int H) {
   const int C = H / 32;
-  for (int cap = 4; cap <= 8; cap *= 2) {
+  if (C >= 256 && C % 64 == 0 && C / 64 <= 4) return 64;
+  for (int cap = 4; cap <= 7; cap += 3) {
     if (C >= 64) {
       for (int lk = 32; lk >= 8; lk /= 2)
         if (C % lk == 0 && C / lk <= cap) return lk;
@@ -1023,7 +1038,6 @@ hipError_t decode_gateup_nb(int nb, Args... args) {
     case 5: return launch_decode_gateup_t<LK, 5>(args...);
     case 6: return launch_decode_gateup_t<LK, 6>(args...);
     case 7: return launch_decode_gateup_t<LK, 7>(args...);
-    case 8: return launch_decode_gateup_t<LK, 8>(args...);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1043,6 +1057,9 @@ hipError_t launch_decode_gateup(const float* logits, const uint16_t* x, const ui
   if (lk == 32)
     return decode_gateup_nb<32>(nb, logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
                                 sorted_slot, slot_pos, active, n_active, h, rec, s);
+  if (lk == 64 && nb == 4)
+    return launch_decode_gateup_t<64, 4>(logits, x, w13, s13, T, H, I, E, k, ids, w, offsets,
+                                         sorted_slot, slot_pos, active, n_active, h, rec, s);
   return hipErrorInvalidValue;
 }
 

@@ -522,7 +522,8 @@ def test_layer_entry_wide_tiles(case):
 
 def test_layer_entry_in_graph_replays():
     """The fused decode layer captured in a HIP graph: every replay matches the
-    eager result (the combine counters are cleared inside the layer each time)."""
+    eager result (the layer keeps no state between calls: its second kernel
+    takes the combine inside each block, with no counters)."""
     import quantized_moe_expert_top_amd as moe
     wl = synth.workload("decode_t2")
     units = [0, 1, 2]

@@ -7,7 +7,7 @@ dispatch), then summed over the kernels one launch of the unit dispatches.
 The result is stored with a hash of the kernel sources it was measured on;
 bench.py reports it only while that hash still matches.
 
-    python -m quantized_moe_expert_top_amd.traffic --workload decode_t2 \\
+    python traffic.py --workload decode_t2 \\
         --calib-fetch C1.csv --calib-write C2.csv --fetch F.csv --write W.csv
 """
 from __future__ import annotations
@@ -20,8 +20,8 @@ import os
 import re
 from collections import defaultdict
 
-HERE = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(HERE)
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "quantized_moe_expert_top_amd", "csrc")
 STORE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_KIB = 262144.0
 
@@ -41,10 +41,9 @@ UNIT_KERNELS = {
 def source_hash() -> str:
     """Hash of every kernel source the library is built from."""
     h = hashlib.sha256()
-    csrc = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
+            with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
