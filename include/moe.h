@@ -199,6 +199,30 @@ MOE_API moe_status moe_layer_w4a16(const moe_shape* shape, const float* logits, 
                             int32_t* slot_pos, int32_t* active, int32_t* n_active,
                             float* y, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_layer_w4a16_noalloc — moe_layer_w4a16 for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments minus the workspace, same kernels and outputs
+ * (bit for bit); the layer's workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing. A shape whose
+ * moe_layer_w4a16_workspace() exceeds MOE_NOALLOC_SCRATCH_BYTES is refused
+ * with MOE_EWORKSPACE before anything is enqueued. Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap in time on one GPU (other streams, other host threads) race, so the
+ * caller must order them. Nothing in the array needs to start at zero (each
+ * call writes what it reads). The first call on a device looks up the array's
+ * address there (MOE_EDEVICE if that fails).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+MOE_API moe_status moe_layer_w4a16_noalloc(const moe_shape* shape, const float* logits,
+                                           const uint16_t* x, const uint8_t* w13,
+                                           const uint16_t* s13, const uint8_t* w2,
+                                           const uint16_t* s2, int32_t* topk_ids, float* topk_w,
+                                           int32_t* expert_offsets, int32_t* sorted_slot,
+                                           int32_t* slot_pos, int32_t* active, int32_t* n_active,
+                                           float* y, float* out, void* stream);
+
 /* Optional W8A8 intermediate outputs (device pointers; any may be NULL). */
 typedef struct {
   int8_t* xq;     /* [T, H]   per-token int8 activations                 */

@@ -11,14 +11,15 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import (  # noqa: F401
     MoeError, combine, expert_counts_accumulate, expert_hot_rank, grouped_w4a16_ffn, grouped_w4a8_ffn, grouped_w8a8_ffn, layer_w4a16,
-    layer_w4a16_workspace, load, permute, permute_workspace, route_topk, router_logits,
+    layer_w4a16_noalloc, layer_w4a16_workspace, load, permute, permute_workspace, route_topk,
+    router_logits,
     w4a16_workspace, w4a8_workspace, w8a8_workspace,
 )
 
 __all__ = ["MoeError", "LayerBuffers", "moe_forward", "moe_layer", "load", "router_logits",
            "route_topk",
            "permute", "grouped_w4a16_ffn", "grouped_w4a8_ffn", "grouped_w8a8_ffn", "combine",
-           "layer_w4a16", "expert_counts_accumulate", "expert_hot_rank"]
+           "layer_w4a16", "layer_w4a16_noalloc", "expert_counts_accumulate", "expert_hot_rank"]
 
 
 @dataclass

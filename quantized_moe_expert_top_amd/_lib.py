@@ -22,7 +22,8 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_abi_version", "moe_router_lo
            "moe_grouped_w4a16_ffn", "moe_w4a8_workspace", "moe_grouped_w4a8_ffn",
            "moe_w8a8_workspace", "moe_grouped_w8a8_ffn", "moe_expert_counts_accumulate",
            "moe_expert_hot_rank",
-           "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16")
+           "moe_combine", "moe_layer_w4a16_workspace", "moe_layer_w4a16",
+           "moe_layer_w4a16_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [P, P, P, I32, I32, I32, P, P]),
         "moe_layer_w4a16_workspace": (SZ, [ctypes.POINTER(MoeShape)]),
         "moe_layer_w4a16": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 16 + [SZ, P]),
+        "moe_layer_w4a16_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeShape)] + [P] * 16),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -306,8 +308,8 @@ def layer_w4a16_workspace(T: int, H: int, I: int, E: int, k: int) -> int:
     return int(load().moe_layer_w4a16_workspace(ctypes.byref(s)))
 
 
-def layer_w4a16(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
-                sorted_slot, slot_pos, active, n_active, y, out, ws, stream=None) -> None:
+def _check_layer_sizes(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                       sorted_slot, slot_pos, active, n_active, y, out) -> None:
     T, H, I, E, k = shape
     R = T * k
     if T > 0 and H % 128 == 0 and I % 128 == 0:
@@ -321,6 +323,24 @@ def layer_w4a16(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_off
         _need(topk_w, R * 4, "topk_w")
         _need(slot_pos, R * 4, "slot_pos")
         _need(out, T * H * 4, "out")
+
+
+def layer_w4a16_noalloc(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                        sorted_slot, slot_pos, active, n_active, y, out, stream=None) -> None:
+    """moe_layer_w4a16 on the library's static scratch (no workspace argument)."""
+    _check_layer_sizes(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                       sorted_slot, slot_pos, active, n_active, y, out)
+    s = MoeShape(*shape)
+    _check("moe_layer_w4a16_noalloc", load().moe_layer_w4a16_noalloc(
+        ctypes.byref(s), _ptr(logits), _ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_slot), _ptr(slot_pos),
+        _ptr(active), _ptr(n_active), _ptr(y), _ptr(out), _stream(stream)))
+
+
+def layer_w4a16(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                sorted_slot, slot_pos, active, n_active, y, out, ws, stream=None) -> None:
+    _check_layer_sizes(shape, logits, x, w13, s13, w2, s2, topk_ids, topk_w, expert_offsets,
+                       sorted_slot, slot_pos, active, n_active, y, out)
     s = MoeShape(*shape)
     nbytes = ws.numel() * ws.element_size()
     _check("moe_layer_w4a16", load().moe_layer_w4a16(

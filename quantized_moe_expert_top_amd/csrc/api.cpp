@@ -84,6 +84,31 @@ moe_status check_shape(const moe_shape* s, int hmod, int imod) {
   return MOE_OK;
 }
 
+// Scratch of moe_layer_w4a16_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends. In host code the array's name is only a
+// host-side stand-in: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current (on the entry point's first call
+// there) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(MOE_EDEVICE, "hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EDEVICE, "device index %d out of range", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return fail(MOE_EDEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(err));
+    g_scratch[dev].store(p, std::memory_order_release);   // racing threads store the same value
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 #define REQUIRE_PTR(p)                                              \
   do {                                                              \
     if (!(p)) return fail(MOE_EINVAL, "%s is NULL", #p);            \
@@ -245,6 +270,47 @@ moe_status moe_layer_w4a16(const moe_shape* s, const float* logits, const uint16
                                           slot_pos, active, n_active, y, out, ws,
                                           static_cast<hipStream_t>(stream)),
                   "moe_layer_w4a16 launch");
+}
+
+moe_status moe_layer_w4a16_noalloc(const moe_shape* s, const float* logits, const uint16_t* x,
+                                   const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
+                                   const uint16_t* s2, int32_t* topk_ids, float* topk_w,
+                                   int32_t* expert_offsets, int32_t* sorted_slot,
+                                   int32_t* slot_pos, int32_t* active, int32_t* n_active,
+                                   float* y, float* out, void* stream) {
+  moe_status st = check_shape(s, MOE_GROUP, MOE_GROUP);
+  if (st) return st;
+  const size_t need = moe::w4a16_layer_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE,
+                "this shape needs %zu bytes of scratch; the static scratch of "
+                "moe_layer_w4a16_noalloc holds %zu (use moe_layer_w4a16 with a workspace)",
+                need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(n_active);
+  if (s->T > 0) {
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(s13);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(s2);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(sorted_slot);
+    REQUIRE_PTR(slot_pos);
+    REQUIRE_PTR(active);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(out);
+  }
+  if ((st = check_device()) != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  return launched(moe::launch_w4a16_layer(s->T, s->H, s->I, s->E, s->k, logits, x, w13, s13, w2,
+                                          s2, topk_ids, topk_w, expert_offsets, sorted_slot,
+                                          slot_pos, active, n_active, y, out, ws,
+                                          static_cast<hipStream_t>(stream)),
+                  "moe_layer_w4a16_noalloc launch");
 }
 
 size_t moe_w4a8_workspace(const moe_shape* s) {

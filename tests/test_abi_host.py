@@ -32,7 +32,7 @@ def header_functions():
 @needs_lib
 def test_exports_match_header():
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(LIB, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -245,3 +245,24 @@ def test_expert_telemetry_validation():
     if _no_gpu():
         assert f(A, 9, 2, 8, A, None) == 6
         assert h(A, 3, 8, 2, A, None) == 6
+
+
+@needs_lib
+def test_layer_w4a16_noalloc_validation():
+    """The no-allocation layer entry: shapes whose workspace exceeds the static
+    scratch are refused before anything else; then the usual checks."""
+    f = LIB.moe_layer_w4a16_noalloc
+    ok = [A] * 15
+    big = _shape(T=4096, H=2048, I=768, E=128, k=8)
+    assert _lib.layer_w4a16_workspace(4096, 2048, 768, 128, 8) > 8 << 20
+    assert f(ctypes.byref(big), *ok, None) == 4
+    assert b"static scratch" in LIB.moe_last_error()
+    s = _shape()
+    assert f(ctypes.byref(_shape(H=200)), *ok, None) == 2
+    bad = list(ok)
+    bad[1] = MIS
+    assert f(ctypes.byref(s), *bad, None) == 3
+    bad[1] = None
+    assert f(ctypes.byref(s), *bad, None) == 1
+    if _no_gpu():
+        assert f(ctypes.byref(s), *ok, None) == 6
