@@ -6,13 +6,22 @@ T=2, H=2048, I=768, E=128, k=8, W4A16 g128, 48 independent layers per step
 (so one step is one decode step through a 48-layer MoE stack). All inputs are
 seeded synthetic tensors resident in HBM before the timed region.
 
-Prints one JSON line with the whole-job throughput (tokens/s), a roofline
-entry for the dominant kernel (the grouped FFN call: gate/up + down), and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line with the whole-job throughput (tokens/s) of the chosen
+workload, a roofline entry for its dominant unit, and the CPU oracle's
+throughput on a bounded sample of the same workload. The default run also
+carries a `prefill` block measured in the same process on the prompt
+workload (T=4096, W8A8 on int8 MFMA): grouped-FFN time per layer, its int8
+MFMA fraction, its HBM fraction and its measured traffic.
+
+Algorithmic bytes per unit (the roofline's numerator) are what the method
+must move: the packed weights and scales of the experts the unit routes to,
+x in, the router logits in and out in. Intermediates (h, the grouped y) are
+overheads of the design and show up only in the measured traffic.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -32,6 +41,7 @@ MFMA_PEAK = {"bf16": 2500.0, "int8": 5000.0}   # dense, TFLOP/s (TOP/s for int8)
 # 16-byte loads, 402.7 MB per kernel): the achievable side of the HBM roofline
 HBM_MEASURED_CEILING_GBS = 6320.0
 METRIC = "MoE-FFN tokens/s; decode HBM GB/s % of peak; prefill MFMA % of peak"
+PREFILL_WORKLOAD = "w8a8_t4096"
 
 
 def parse():
@@ -41,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prompt-workload block of the default run")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of HIP graphs")
     ap.add_argument("--path", choices=("layer", "calls"), default=None,
                     help="layer: moe_layer_w4a16 (one call per layer; W4A16 only); "
@@ -49,7 +61,34 @@ def parse():
     ap.add_argument("--units", type=int, default=None,
                     help="stage only the first N units (short counter passes; per-launch "
                          "figures do not depend on the number of units)")
+    ap.add_argument("--mark", action="store_true",
+                    help="wrap each timed region in a roctx range (for kernel traces)")
     return ap.parse_args()
+
+
+class Marker:
+    """roctx ranges around timed regions (no-ops unless --mark and a roctx
+    library loads); a kernel trace taken with --marker-trace can then keep
+    only the dispatches inside them."""
+
+    def __init__(self, on: bool):
+        self.lib = None
+        if on:
+            for name in ("librocprofiler-sdk-roctx.so.1", "/opt/rocm/lib/librocprofiler-sdk-roctx.so.1",
+                         "libroctx64.so", "/opt/rocm/lib/libroctx64.so"):
+                try:
+                    self.lib = ctypes.CDLL(name)
+                    break
+                except OSError:
+                    continue
+
+    def push(self, label: str):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(label.encode())
+
+    def pop(self):
+        if self.lib is not None:
+            self.lib.roctxRangePop()
 
 
 def stage(wl, torch):
@@ -80,6 +119,12 @@ def expert_bytes(wl) -> int:
     return 2 * wl.I * wl.H + 2 * wl.I * 4 + wl.H * wl.I + wl.H * 4
 
 
+def io_bytes(wl) -> int:
+    """Layer I/O the method must move besides weights: x (bf16), router
+    logits (float32) and out (float32)."""
+    return wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 4
+
+
 def layers_per_step(wl) -> list:
     """Units one step runs: every layer (decode/prefill stacks) or one unit."""
     if wl.name in ("decode_t2", "prefill_t512"):
@@ -87,20 +132,9 @@ def layers_per_step(wl) -> list:
     return [[u] for u in range(wl.units)]
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import quantized_moe_expert_top_amd as moe
-
-    torch.cuda.set_device(0)
-    moe.load()
-    wl = synth.workload(args.workload)
-    if args.units:
-        wl = wl.with_(units=min(args.units, wl.units))
+def measure(wl, args, torch, moe, marker, path=None):
+    """Stage the workload, time K steps of the whole path (HIP graph per step
+    unless --eager), then its dominant unit; returns the figures."""
     units = stage(wl, torch)
     bufs = [moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, wl.fmt) for _ in range(wl.units)]
     shape = (wl.T, wl.H, wl.I, wl.E, wl.k)
@@ -114,7 +148,7 @@ def main():
         ffn(shape, x, w13, s13, w2, s2, b.offsets, b.sorted_slot, b.active, b.n_active, b.y,
             b.ffn_ws)
 
-    path = args.path or ("layer" if wl.fmt == "w4a16" else "calls")
+    path = path or ("layer" if wl.fmt == "w4a16" else "calls")
     if path == "layer" and wl.fmt != "w4a16":
         raise SystemExit("--path layer covers W4A16 workloads")
 
@@ -178,6 +212,7 @@ def main():
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    marker.push(f"timed_steps {wl.name}")
     t0.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -185,9 +220,9 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    marker.pop()
     ms_total = t0.elapsed_time(t1)
     ms_per_step = ms_total / args.steps
-    value = wl.T * args.steps / (ms_total / 1e3)   # each step carries T tokens
 
     # spread: three more passes of K steps each, after the timed region
     pass_ms = []
@@ -205,6 +240,7 @@ def main():
 
     # cold-cache steps (large-expert decode): a 1 GiB write between steps,
     # outside the timed window, evicts the 256 MB MALL before each step
+    cold_ms = None
     if wl.name == "decode_large" and not args.eager:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         cold = []
@@ -218,95 +254,82 @@ def main():
             torch.cuda.synchronize()
             cold.append(c0.elapsed_time(c1))
         del scratch
-        spread["cold_median_ms_per_step"] = round(float(np.median(cold)), 4)
+        cold_ms = float(np.median(cold))
+        spread["cold_median_ms_per_step"] = round(cold_ms, 4)
         spread["warm_ms_per_step"] = round(ms_per_step, 4)
 
-    def time_launches(fn, n=50):
-        """Average device time of fn() over n launches, replayed from a graph
-        (device time, not the host launch rate) unless --eager."""
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        g = None
-        if not args.eager:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(n):
-                    fn()
-            g.replay()
-            torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        if g is not None:
-            g.replay()
-        else:
-            for _ in range(n):
-                fn()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e3 / n
-
-    # the router projection ahead of the top-k (logits = x . w_r^T) on this
-    # workload's shape, timed alone: a separate row, not part of the step
-    wr = torch.from_numpy(synth.router_weights(wl, 0).view(np.int16)).cuda()
-    x0 = units[0][0]
-    lg = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
-    router_us = time_launches(lambda: moe.router_logits(x0, wr, lg))
-    router_bytes = wl.T * wl.H * 2 + wl.E * wl.H * 2 + wl.T * wl.E * 4
-    router_row = {"kernel": "router_logits_kernel (moe_router_logits)",
-                  "avg_launch_us": round(router_us, 2),
-                  "algo_bytes_per_launch": router_bytes,
-                  "achieved_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
-                  "flops_per_launch": 2 * wl.T * wl.H * wl.E}
-
-    # expert-load telemetry over one step's layers: their expert_offsets
-    # gathered into one [L, E + 1] array, counts accumulated in one launch,
-    # then each layer's 16 most-loaded experts ranked (a separate row)
-    step_units = schedule[0]
-    offs = torch.stack([bufs[u].offsets[:wl.E + 1] for u in step_units])
-    loads = torch.zeros((len(step_units), wl.E), dtype=torch.int64, device="cuda")
-    n_hot = min(16, wl.E)
-    hot = torch.empty((len(step_units), n_hot), dtype=torch.int32, device="cuda")
-    counts_us = time_launches(lambda: moe.expert_counts_accumulate(offs, loads))
-    hot_us = time_launches(lambda: moe.expert_hot_rank(loads, n_hot, hot))
-    telemetry_row = {"kernels": "expert_counts_kernel, hot_rank_kernel "
-                                "(moe_expert_counts_accumulate, moe_expert_hot_rank)",
-                     "layers": len(step_units), "hot_n": n_hot,
-                     "counts_avg_launch_us": round(counts_us, 2),
-                     "hot_rank_avg_launch_us": round(hot_us, 2)}
-
     calls = [u for i in range(args.steps) for u in schedule[i % len(schedule)]]
-    eb = expert_bytes(wl)
     if path == "layer":
         # dominant unit: the whole-layer call (its kernels carry all of the
         # layer's bytes); per-call time from the timed region itself
         avg_ms = ms_total / len(calls)
-        io_bytes = wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 4  # x, logits, out
         kernel = ("moe_layer_w4a16 (whole layer: fused decode gate/up + down kernels)"
                   if wl.T <= 4 else
                   "moe_layer_w4a16 (whole layer: route, permute, grouped MFMA FFN, combine)")
     else:
-        # dominant kernel: the grouped FFN calls of the same K steps, back to
+        # dominant unit: the grouped FFN calls of the same K steps, back to
         # back on the same stream, timed with HIP events
         f0 = torch.cuda.Event(enable_timing=True)
         f1 = torch.cuda.Event(enable_timing=True)
+        marker.push(f"timed_ffn {wl.name}")
         f0.record(stream)
         for i in range(args.steps):
             run_ffn(i)
         f1.record(stream)
         torch.cuda.synchronize()
+        marker.pop()
         avg_ms = f0.elapsed_time(f1) / len(calls)
-        io_bytes = wl.T * wl.H * 2 + wl.T * wl.k * wl.H * 4   # x in (bf16), y out (float32)
         kernel = f"moe_grouped_{wl.fmt}_ffn (gate/up + down kernels)"
-    avg_bytes = sum(act_per_unit[u] * eb + io_bytes for u in calls) / len(calls)
-    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
+    eb = expert_bytes(wl)
+    avg_bytes = sum(act_per_unit[u] * eb + io_bytes(wl) for u in calls) / len(calls)
     flops_per_call = 6.0 * wl.H * wl.I * wl.T * wl.k
-    # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
-    # a copy of known size), valid only for the kernel sources they were taken on
+    return {
+        "wl": wl, "path": path, "schedule": schedule, "units": units, "bufs": bufs,
+        "ms_total": ms_total, "ms_per_step": ms_per_step, "wall": wall, "spread": spread,
+        "cold_ms": cold_ms, "avg_ms": avg_ms, "avg_bytes": avg_bytes, "kernel": kernel,
+        "flops_per_call": flops_per_call,
+        "mean_active": float(np.mean(list(act_per_unit.values()))),
+        "time_launches": lambda fn, n=50: time_launches(fn, args, torch, stream, n),
+    }
+
+
+def time_launches(fn, args, torch, stream, n=50):
+    """Average device time of fn() over n launches, replayed from a graph
+    (device time, not the host launch rate) unless --eager."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    g = None
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for _ in range(n):
+            fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / n
+
+
+def roofline(m) -> dict:
+    """Roofline entry of the dominant unit: algorithmic bytes of the unit over
+    its average duration against the HBM peak, the MFMA fraction beside it for
+    the GEMM-shaped workloads, and the measured HBM traffic per launch (while
+    it was taken on the current kernel sources)."""
     import traffic as traffic_store
+    wl = m["wl"]
+    achieved = m["avg_bytes"] / (m["avg_ms"] / 1e3) / 1e9
     tr = traffic_store.lookup(wl.name)
-    roofline = {
+    out = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
@@ -314,15 +337,94 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "frac_of_measured_ceiling": round(achieved / HBM_MEASURED_CEILING_GBS, 4),
         "traffic": tr["bytes_per_launch"] if tr else None,
-        "kernel": kernel,
-        "avg_launch_us": round(avg_ms * 1e3, 2),
-        "algo_bytes_per_launch": int(avg_bytes),
+        "kernel": m["kernel"],
+        "avg_launch_us": round(m["avg_ms"] * 1e3, 2),
+        "algo_bytes_per_launch": int(m["avg_bytes"]),
     }
+    if m["cold_ms"] is not None:
+        # the large-expert decode shares one layer's weights across its steps:
+        # back-to-back steps can find hot experts in the 256 MB MALL, so the
+        # HBM fraction is also given for steps after a 1 GiB write
+        cold_achieved = m["avg_bytes"] / (m["cold_ms"] / 1e3) / 1e9
+        out["frac_cold"] = round(cold_achieved / HBM_PEAK_GBS, 4)
     if wl.fmt != "w4a16" or wl.T >= 512:
         dt = "bf16" if wl.fmt == "w4a16" else "int8"
-        roofline["mfma_frac"] = round(flops_per_call / (avg_ms / 1e3) / 1e12 / MFMA_PEAK[dt], 4)
+        out["mfma_frac"] = round(m["flops_per_call"] / (m["avg_ms"] / 1e3) / 1e12 / MFMA_PEAK[dt], 4)
+    return out
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, schedule, args.cpu_budget_s)
+
+def side_rows(m, torch, moe):
+    """Router projection and expert-load telemetry on the workload's shape,
+    timed alone: separate rows, not part of the step."""
+    wl, bufs, units = m["wl"], m["bufs"], m["units"]
+    tl = m["time_launches"]
+    wr = torch.from_numpy(synth.router_weights(wl, 0).view(np.int16)).cuda()
+    x0 = units[0][0]
+    lg = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
+    router_us = tl(lambda: moe.router_logits(x0, wr, lg))
+    router_bytes = wl.T * wl.H * 2 + wl.E * wl.H * 2 + wl.T * wl.E * 4
+    router_row = {"kernel": "router_logits_kernel (moe_router_logits)",
+                  "avg_launch_us": round(router_us, 2),
+                  "algo_bytes_per_launch": router_bytes,
+                  "achieved_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
+                  "flops_per_launch": 2 * wl.T * wl.H * wl.E}
+    # one step's layers: their expert_offsets gathered into one [L, E + 1]
+    # array, counts accumulated in one launch, each layer's 16 most-loaded
+    # experts ranked
+    step_units = m["schedule"][0]
+    offs = torch.stack([bufs[u].offsets[:wl.E + 1] for u in step_units])
+    loads = torch.zeros((len(step_units), wl.E), dtype=torch.int64, device="cuda")
+    n_hot = min(16, wl.E)
+    hot = torch.empty((len(step_units), n_hot), dtype=torch.int32, device="cuda")
+    counts_us = tl(lambda: moe.expert_counts_accumulate(offs, loads))
+    hot_us = tl(lambda: moe.expert_hot_rank(loads, n_hot, hot))
+    telemetry_row = {"kernels": "expert_counts_kernel, hot_rank_kernel "
+                                "(moe_expert_counts_accumulate, moe_expert_hot_rank)",
+                     "layers": len(step_units), "hot_n": n_hot,
+                     "counts_avg_launch_us": round(counts_us, 2),
+                     "hot_rank_avg_launch_us": round(hot_us, 2)}
+    return router_row, telemetry_row
+
+
+def prefill_block(m) -> dict:
+    """The prompt half of the metric: the grouped W8A8 FFN at T 4096."""
+    wl = m["wl"]
+    r = roofline(m)
+    return {
+        "workload": wl.name,
+        "config": {"T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k, "format": "W8A8",
+                   "layers_rotated": wl.units},
+        "tokens_per_s": round(wl.T / (m["ms_per_step"] / 1e3), 1),
+        "layer_us": round(m["ms_per_step"] * 1e3, 2),
+        "ffn_us": r["avg_launch_us"],
+        "mfma_frac": r["mfma_frac"],
+        "mfma_peak_TOPs": MFMA_PEAK["int8"],
+        "hbm_frac": r["frac"],
+        "algo_bytes_per_launch": r["algo_bytes_per_launch"],
+        "traffic": r["traffic"],
+        "kernel": r["kernel"],
+        "spread_median_layer_us": round(m["spread"]["median_ms_per_step"] * 1e3, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_moe_expert_top_amd as moe
+
+    torch.cuda.set_device(0)
+    moe.load()
+    marker = Marker(args.mark)
+    wl = synth.workload(args.workload)
+    if args.units:
+        wl = wl.with_(units=min(args.units, wl.units))
+    m = measure(wl, args, torch, moe, marker, args.path)
+    router_row, telemetry_row = side_rows(m, torch, moe)
+    value = wl.T / (m["ms_per_step"] / 1e3)   # each step carries T tokens
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -330,26 +432,36 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(m["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.fmt == "w4a16" else "int8",
         "data": "synthetic (seeded; random int4/int8 expert weights, N(0,1) activations)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
-                   "format": {"w4a16": "W4A16 g128", "w4a8": "W4A8 (int4 g128 weights, int8 per-token activations)",
+                   "format": {"w4a16": "W4A16 g128",
+                              "w4a8": "W4A8 (int4 g128 weights, int8 per-token activations)",
                               "w8a8": "W8A8"}[wl.fmt],
-                   "layers_per_step": len(schedule[0]),
+                   "layers_per_step": len(m["schedule"][0]),
                    "launch": "eager" if args.eager else "hip_graph_per_step",
-                   "path": path,
-                   "mean_active_experts": round(float(np.mean(list(act_per_unit.values()))), 2)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "spread": spread,
+                   "path": m["path"],
+                   "mean_active_experts": round(m["mean_active"], 2)},
+        "roofline": roofline(m),
+        "cpu_baseline": None,
+        "spread": m["spread"],
         "router_projection": router_row,
         "expert_load_telemetry": telemetry_row,
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(m["wall"], 3),
     }
+    if args.workload == "decode_t2" and not args.no_prefill and not args.units:
+        del m
+        torch.cuda.empty_cache()
+        p = measure(synth.workload(PREFILL_WORKLOAD), args, torch, moe, marker)
+        line["prefill"] = prefill_block(p)
+        del p
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, layers_per_step(wl), args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 
