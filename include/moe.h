@@ -247,8 +247,9 @@ typedef struct {
  *   y[p, m] = acc2[p, m] * hs[p] * s2[e, m]                  (float32)
  *   x   bf16 [T, H]; w13 int8 [E, 2I, H], s13 float32 [E, 2I];
  *   w2  int8 [E, H, I], s2 float32 [E, H]; y float32 [T*k, H] (grouped order).
- * Requires H % 64 == 0, I % 64 == 0. `dbg` may be NULL; non-NULL members
- * receive the intermediates. `ws` must hold moe_w8a8_workspace(shape) bytes.
+ * Requires H % 16 == 0, I % 16 == 0 (K tails shorter than the GEMM's 64-wide
+ * stage are zero-filled). `dbg` may be NULL; non-NULL members receive the
+ * intermediates. `ws` must hold moe_w8a8_workspace(shape) bytes.
  */
 MOE_API size_t moe_w8a8_workspace(const moe_shape* shape);
 MOE_API moe_status moe_grouped_w8a8_ffn(const moe_shape* shape, const uint16_t* x,

@@ -270,7 +270,7 @@ def grouped_w8a8_ffn(shape, x, w13, s13, w2, s2, expert_offsets, sorted_slot, ac
                      n_active, y, ws, debug: dict | None = None, stream=None) -> None:
     T, H, I, E, k = shape
     R = T * k
-    if T > 0 and H % 64 == 0 and I % 64 == 0:
+    if T > 0 and H % 16 == 0 and I % 16 == 0:
         _check_ffn_sizes(shape, x, expert_offsets, sorted_slot, active, n_active, y)
         _need(w13, E * 2 * I * H, "w13")
         _need(s13, E * 2 * I * 4, "s13")

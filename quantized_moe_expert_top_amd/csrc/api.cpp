@@ -354,7 +354,7 @@ moe_status moe_grouped_w4a8_ffn(const moe_shape* s, const uint16_t* x, const uin
 }
 
 size_t moe_w8a8_workspace(const moe_shape* s) {
-  if (check_shape(s, 64, 64)) return 0;
+  if (check_shape(s, 16, 16)) return 0;
   return moe::w8a8_workspace_bytes(s->T, s->H, s->I, s->E, s->k);
 }
 
@@ -363,7 +363,7 @@ moe_status moe_grouped_w8a8_ffn(const moe_shape* s, const uint16_t* x, const int
                          const int32_t* expert_offsets, const int32_t* sorted_slot,
                          const int32_t* active, const int32_t* n_active, float* y,
                          const moe_w8a8_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_shape(s, 64, 64);
+  moe_status st = check_shape(s, 16, 16);
   if (st) return st;
   if (s->T == 0) return MOE_OK;
   REQUIRE_PTR(x);

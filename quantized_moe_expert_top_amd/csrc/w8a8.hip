@@ -20,7 +20,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;        // rows per tile
+constexpr int kW8BM = 128;      // rows per GEMM tile (two blocks per CU; 256 measured slower)
 constexpr int kBK = 64;         // K per pipeline step (two MFMA k-steps of 32)
 
 // --------------------------------------------------------- quantization ----
@@ -174,12 +174,16 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------- int8 GEMM ----
-// KIND 0: gate/up. Tile = 128 rows x 128 h-columns: the B tile holds the 128
+// A block has BM/64 x 2 waves (BM * 2 threads); each wave owns 64 tile rows
+// and 128 B rows (two 32-row by four 32-column MFMA subtiles).
+// KIND 0: gate/up. Tile = BM rows x 128 h-columns: the B tile holds the 128
 //         gate rows and the 128 matching up rows (256 W13 rows). Wave (wm, wn)
-//         owns rows [64wm, +64) and h-columns [64wn, +64): subtiles 0,1 gate,
-//         2,3 the matching up rows. Out: h float32 [R, I].
-// KIND 1: down. Tile = 128 rows x 256 W2 rows; wave (wm, wn) owns rows
+//         owns rows [64wm, +64) and h-columns [64wn, +64): subtiles 0,1
+//         gate, 2,3 the matching up rows. Out: h float32 [R, I].
+// KIND 1: down. Tile = BM rows x 256 W2 rows; wave (wm, wn) owns rows
 //         [64wm, +64) and W2 rows [128wn, +128) as four subtiles. Out: y.
+// BM = 128: 256 threads, two blocks per CU. BM = 256: 512 threads, one block
+// per CU, each B strip staged once for twice the rows.
 // Pipeline: K advances in 64-byte stages; kW8Stages stages are in flight,
 // each moved HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging;
 // the buffer form, unlike the global one, leaves LDS reads countable in order,
@@ -188,37 +192,65 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 // row s/4, chunk (s%4) ^ ((row/4)%4), so each row's 64 bytes are still read as
 // one coalesced run while the MFMA operand reads (32 rows, one chunk each) hit
 // distinct LDS banks. Waits are explicit (vmcnt + barrier) so loads of later
-// stages stay in flight across the barrier.
+// stages stay in flight across the barrier: each stage is exactly
+// kLoadsPerStage vector-memory instructions per thread and nothing else in
+// the loop touches vector memory (the library build rejects any kernel that
+// spills to scratch, which would add such instructions).
 // MFMA operand k order inside one 32-k step: lane half hf = lane/32 takes
 // k = 32*ks + 16*hf + [0, 16).
 constexpr int kW8Stages = 3;
 constexpr int kW8BN = 256;                       // B rows per tile
-constexpr int kW8ASlots = kBM * 4;               // 16-byte slots per stage
 constexpr int kW8BSlots = kW8BN * 4;
-constexpr int kW8StageBytes = (kW8ASlots + kW8BSlots) * 16;
 
 __device__ __forceinline__ int swz(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
-template <int KIND>
-__global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
+// s_waitcnt vmcnt(N) then s_barrier, for the counts the pipeline uses
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N == 0 || N == 4 || N == 6 || N == 8 || N == 12 || N == 16, "add the count here");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM>
+struct W8Geom {
+  static constexpr int kThreads = BM * 2;
+  static constexpr int kASlots = BM * 4;                       // 16-byte A slots per stage
+  static constexpr int kStageBytes = (kASlots + kW8BSlots) * 16;
+  static constexpr int kAPer = kASlots / kThreads;              // A loads per thread per stage
+  static constexpr int kBPer = kW8BSlots / kThreads;
+  static constexpr int kLoadsPerStage = kAPer + kBPer;
+  static constexpr int kMI = 2;                                 // 32-row subtiles per wave
+  static constexpr int kBlocksPerCU = BM == 128 ? 2 : 1;
+};
+
+template <int KIND, int BM>
+__global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) void w8a8_mfma_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const int8_t* __restrict__ W, const float* __restrict__ w_scale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_slot, int a_rows, int K,
     int N, int E, int topk, int NT, float* __restrict__ h_out, float* __restrict__ y_out,
     int32_t* __restrict__ dbg_acc) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // kW8Stages * kW8StageBytes
-  __shared__ int row_src[kBM];
-  __shared__ float row_scale[kBM];    // activation scale of each tile row
+  using G = W8Geom<BM>;
+  constexpr int MI = G::kMI;
+  constexpr int NTHR = G::kThreads;
+  extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // kW8Stages * kStageBytes
+  __shared__ int row_src[BM];
+  __shared__ float row_scale[BM];     // activation scale of each tile row
   __shared__ float col_scale[kW8BN];  // weight scale of each B tile row
-  __shared__ int sm_pref[kThreads / kWave];
+  __shared__ int sm_pref[NTHR / kWave];
   __shared__ int sm_out[5];
 
   TileInfo ti;
-  if (!find_tile<kBM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
+  if (!find_tile<BM, NTHR>(offsets, E, NT, sm_pref, sm_out, ti)) return;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 1, wn = wv & 1;   // wave's 64-row band and B half
   const int I = N / 2;  // KIND 0 only
 
   // W row held at B tile row j (0..255)
@@ -233,55 +265,67 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
   // source row of each A tile row (token for gate/up, grouped row for down);
   // rows past the expert's block read the tile's first row (results dropped).
   // The scales the epilogue needs are staged here, off its critical path.
-  if (tid < kBM) {
-    const int p = ti.p_begin + tid;
+  for (int r = tid; r < BM; r += NTHR) {
+    const int p = ti.p_begin + r;
     const int pv = (p < ti.p_end) ? p : ti.p_begin;
     const int src = (KIND == 0) ? sorted_slot[pv] / topk : pv;
-    row_src[tid] = src;
-    row_scale[tid] = a_scale[src];
+    row_src[r] = src;
+    row_scale[r] = a_scale[src];
   }
-  col_scale[tid] = w_scale[static_cast<size_t>(ti.e) * N + b_row(tid)];
+  if (tid < kW8BN) col_scale[tid] = w_scale[static_cast<size_t>(ti.e) * N + b_row(tid)];
   __syncthreads();
 
-  // this thread's 2 A and 4 B slots per stage (slot = wave * 64 + lane + 256 * v),
+  // this thread's A and B slots per stage (slot = wave * 64 + lane + NTHR * v),
   // as byte offsets into buffer resources over A and this expert's W rows
   const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(A, static_cast<uint32_t>(a_rows) * K);
   const __amdgpu_buffer_rsrc_t b_rsrc =
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * K, static_cast<uint32_t>(N) * K);
-  uint32_t aoff[2], boff[4];
+  // fixed-size arrays: a lambda capturing arrays whose size depends on the
+  // template parameters makes the host pass drop the kernel's launch stub
+  static_assert(G::kAPer <= 4 && G::kBPer <= 4, "slot arrays hold four per thread");
+  uint32_t aoff[4], boff[4], akc[4], bkc[4];   // row offset + chunk, and the chunk's k
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int s = tid + kThreads * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+  for (int v = 0; v < G::kAPer; ++v) {
+    const int s = tid + NTHR * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
     aoff[v] = static_cast<uint32_t>(row_src[row]) * K + c * 16;
+    akc[v] = c * 16;
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int s = tid + kThreads * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+  for (int v = 0; v < G::kBPer; ++v) {
+    const int s = tid + NTHR * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
     boff[v] = static_cast<uint32_t>(b_row(row)) * K + c * 16;
+    bkc[v] = c * 16;
   }
+  // K % 64 may be 16, 32 or 48: the last stage's chunks past K read at an
+  // offset past the buffer's end, which the hardware returns as zeros (an
+  // exact zero term in every dot product)
+  constexpr uint32_t kPastEnd = 0x80000000u;   // beyond any buffer resource here
+  const uint32_t Ku = static_cast<uint32_t>(K);
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   auto issue = [&](int st) {
-    uint8_t* base = w8_lds + (st % kW8Stages) * kW8StageBytes + wvu * kWave * 16;
+    uint8_t* base = w8_lds + (st % kW8Stages) * G::kStageBytes + wvu * kWave * 16;
     const uint32_t k0 = static_cast<uint32_t>(st) * kBK;
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_t*)(base + kThreads * v * 16), 16,
-                                               aoff[v] + k0, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < G::kAPer; ++v)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (lds_void_t*)(base + (kW8ASlots + kThreads * v) * 16), 16, boff[v] + k0, 0, 0, 0);
+          a_rsrc, (lds_void_t*)(base + NTHR * v * 16), 16,
+          k0 + akc[v] < Ku ? aoff[v] + k0 : kPastEnd, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < G::kBPer; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          b_rsrc, (lds_void_t*)(base + (G::kASlots + NTHR * v) * 16), 16,
+          k0 + bkc[v] < Ku ? boff[v] + k0 : kPastEnd, 0, 0, 0);
   };
 
-  i32x16_t acc[2][4];
+  i32x16_t acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  const int steps = K / kBK;
+  const int steps = (K + kBK - 1) / kBK;
   // land the epilogue's kernel arguments now: a scalar load still in flight
   // inside the loop would turn every LDS wait there into a full drain
   asm volatile("" ::"s"(h_out), "s"(y_out), "s"(dbg_acc));
@@ -289,22 +333,22 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
   for (int st = 0; st < kW8Stages - 1; ++st)
     if (st < steps) issue(st);
 
+  static_assert(kW8Stages == 3, "the waits below assume at most two stages ahead");
   for (int st = 0; st < steps; ++st) {
     // stage st is complete once at most the later in-flight stages remain
     const int later = min(kW8Stages - 2, steps - 1 - st);
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (later >= 1) wait_vm_barrier<G::kLoadsPerStage>();
+    else wait_vm_barrier<0>();
     if (st + kW8Stages - 1 < steps) issue(st + kW8Stages - 1);
-    const uint8_t* base = w8_lds + (st % kW8Stages) * kW8StageBytes;
+    const uint8_t* base = w8_lds + (st % kW8Stages) * G::kStageBytes;
     // all operand reads of the stage first: the second k-step's reads land
     // while the first k-step's MFMAs run
-    i32x4_t aop[kBK / 32][2], bop[kBK / 32][4];
+    i32x4_t aop[kBK / 32][MI], bop[kBK / 32][4];
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
       const int c = 2 * ks + hf;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int arow = wm * 64 + i * 32 + l32;
         aop[ks][i] = *reinterpret_cast<const i32x4_t*>(base + swz(arow, c) * 16);
       }
@@ -312,19 +356,19 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
       for (int j = 0; j < 4; ++j) {
         const int brow = (KIND == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32)
                                      : (wn * 128 + j * 32 + l32);
-        bop[ks][j] = *reinterpret_cast<const i32x4_t*>(base + (kW8ASlots + swz(brow, c)) * 16);
+        bop[ks][j] = *reinterpret_cast<const i32x4_t*>(base + (G::kASlots + swz(brow, c)) * 16);
       }
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[ks][i], bop[ks][j], acc[i][j], 0, 0, 0);
-    // keep that order through scheduling: 12 LDS reads, then 16 MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    // keep that order through scheduling: the stage's LDS reads, then its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + 4), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * 4, 0);
   }
 
   // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4)
@@ -336,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
     cs[j] = col_scale[brow];
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = wm * 64 + i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
@@ -371,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_mfma_kernel(
   }
 }
 
-template <int KIND>
+template <int KIND, int BM>
 hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t* W,
                             const float* w_scale, const int* offsets, const int* sorted_slot,
                             int K, int N, int E, int topk, int T, float* h_out, float* y_out,
@@ -379,15 +423,15 @@ hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t*
   const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + kW8BN - 1) / kW8BN;
   const long long R = static_cast<long long>(T) * topk;
   const long long act = R < E ? R : E;
-  const long long mt_up = (R + kBM - 1) / kBM + act;
+  const long long mt_up = (R + BM - 1) / BM + act;
   long long grid = (mt_up * NT + 7) / 8 * 8;
-  const size_t lds = static_cast<size_t>(kW8Stages) * kW8StageBytes;
+  const size_t lds = static_cast<size_t>(kW8Stages) * W8Geom<BM>::kStageBytes;
   const hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w8a8_mfma_kernel<KIND>),
+      reinterpret_cast<const void*>(&w8a8_mfma_kernel<KIND, BM>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((w8a8_mfma_kernel<KIND>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     lds, s, A, a_scale, W, w_scale, offsets, sorted_slot,
+  hipLaunchKernelGGL((w8a8_mfma_kernel<KIND, BM>), dim3(static_cast<unsigned>(grid)),
+                     dim3(W8Geom<BM>::kThreads), lds, s, A, a_scale, W, w_scale, offsets, sorted_slot,
                      static_cast<int>(KIND == 0 ? T : R), K, N, E, topk, NT, h_out, y_out, dbg_acc);
   return hipGetLastError();
 }
@@ -437,15 +481,15 @@ hipError_t launch_w8a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
       x, T, H, w.xq, w.xs, dbg.xq, dbg.xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_w8a8_gemm<0>(w.xq, w.xs, w13, s13, offsets, sorted_slot, H, 2 * I, E, k, T, w.h,
-                            nullptr, dbg.acc13, s);
+  err = launch_w8a8_gemm<0, kW8BM>(w.xq, w.xs, w13, s13, offsets, sorted_slot, H, 2 * I, E, k, T,
+                                   w.h, nullptr, dbg.acc13, s);
   if (err != hipSuccess) return err;
   h_quant_kernel<<<(R + rows_per_block - 1) / rows_per_block, kThreads, 0, s>>>(
       w.h, R, I, w.hq, w.hs, dbg.hq, dbg.hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_w8a8_gemm<1>(w.hq, w.hs, w2, s2, offsets, sorted_slot, I, H, E, k, T, nullptr, y,
-                             dbg.acc2, s);
+  return launch_w8a8_gemm<1, kW8BM>(w.hq, w.hs, w2, s2, offsets, sorted_slot, I, H, E, k, T,
+                                    nullptr, y, dbg.acc2, s);
 }
 
 }  // namespace moe

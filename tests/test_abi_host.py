@@ -147,11 +147,13 @@ def test_w4a8_validation():
 
 def test_w8a8_validation():
     f = LIB.moe_grouped_w8a8_ffn
-    s = _shape(H=192, I=64)          # W8A8 needs multiples of 64 only
-    need = _lib.w8a8_workspace(4, 192, 64, 8, 2)
+    s = _shape(H=208, I=48)          # W8A8 needs multiples of 16 only
+    need = _lib.w8a8_workspace(4, 208, 48, 8, 2)
     assert need > 0
     ok = [A] * 10
     assert f(ctypes.byref(_shape(H=100)), *ok, None, A, need, None) == 2
+    assert f(ctypes.byref(_shape(H=208, I=40)), *ok, None, A, need, None) == 2
+    assert _lib.w8a8_workspace(4, 200, 48, 8, 2) == 0      # H % 16 != 0: no workspace size
     assert f(ctypes.byref(s), *ok, None, A, need - 1, None) == 4
     dbg = _lib.MoeW8A8Debug(A, MIS, None, None, None, None)
     assert f(ctypes.byref(s), *ok, ctypes.byref(dbg), A, need, None) == 3
@@ -266,3 +268,18 @@ def test_layer_w4a16_noalloc_validation():
     assert f(ctypes.byref(s), *bad, None) == 1
     if _no_gpu():
         assert f(ctypes.byref(s), *ok, None) == 6
+
+
+@needs_lib
+def test_library_leaves_no_kernel_symbol_undefined():
+    """Every launch stub the host code references is defined in libmoe.so (a
+    kernel whose host stub the compiler drops still links into a shared
+    library, and fails only when the library is loaded)."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-C", "-u", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    missing = [ln for ln in out.splitlines() if "moe::" in ln]
+    assert not missing, "\n".join(missing)

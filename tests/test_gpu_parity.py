@@ -258,6 +258,8 @@ CUSTOM_W8 = [
     ("w8_t1", 203, 1, 128, 64, 4, 1),
     ("w8_many_rows", 204, 700, 256, 128, 4, 2),   # >128 rows per expert
     ("w8_e1024", 206, 40, 256, 128, 1024, 32),    # most experts hold one row
+    ("w8_k_tail_16_48", 207, 37, 208, 176, 8, 2),  # H % 64 = 16, I % 64 = 48: zero-filled tails
+    ("w8_k_tail_32", 208, 20, 160, 96, 8, 3),       # H % 64 = I % 64 = 32
 ]
 
 
