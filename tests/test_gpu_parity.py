@@ -553,12 +553,45 @@ def test_layer_entry_in_graph_replays():
             np.testing.assert_array_equal(to_np(b.out).view(np.uint32), eager[i])
 
 
+def test_full_decode_step_graph_replays_match_eager():
+    """The step bench.py times: all 48 layers of decode_t2 captured in one HIP
+    graph; three replays (with eager work and synchronizations between them)
+    match the eager pass bit for bit in every layer's out."""
+    import quantized_moe_expert_top_amd as moe
+    wl = synth.workload("decode_t2")
+    bufs, ins = [], []
+    for u in range(wl.units):
+        x, L = synth.x_bf16(wl, u), synth.router_logits(wl, u)
+        active = oracle.permute(oracle.route_topk(L, wl.k)[0], wl.E)["active"]
+        ins.append((to_dev(x), to_dev(L), stage_weights(wl, u, active)))
+        bufs.append(moe.LayerBuffers.alloc(wl.T, wl.H, wl.I, wl.E, wl.k, "w4a16"))
+    _say("48-layer step graph", wl.name)
+    for b, (x, L, w) in zip(bufs, ins):
+        moe.moe_layer(b, x, L, w)
+    torch.cuda.synchronize()
+    eager = [to_np(b.out).view(np.uint32).copy() for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b, (x, L, w) in zip(bufs, ins):
+            moe.moe_layer(b, x, L, w)
+    for rep in range(3):
+        for b in bufs:
+            b.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for u, b in enumerate(bufs):
+            np.testing.assert_array_equal(to_np(b.out).view(np.uint32), eager[u],
+                                          err_msg=f"replay {rep}, layer {u}")
+
+
 # ------------------------------------------------------- batch invariance --
 INVARIANCE_CASES = [
     # T, tokens per sub-batch, path (layer entry: fused decode; calls: MFMA GEMM)
     (4, 1, "layer"),   # persistent gate/up for the batch, slot-per-block alone
     (4, 2, "layer"),
     (40, 20, "calls"),
+    (512, 128, "calls"),   # the prompt shape on the MFMA GEMMs, against four batches of 128
 ]
 
 
