@@ -127,7 +127,7 @@ def io_bytes(wl) -> int:
 
 def layers_per_step(wl) -> list:
     """Units one step runs: every layer (decode/prefill stacks) or one unit."""
-    if wl.name in ("decode_t2", "prefill_t512"):
+    if wl.name in ("decode_t2", "prefill_t512", "prefill_t512_flat"):
         return [list(range(wl.units))]
     return [[u] for u in range(wl.units)]
 
@@ -169,6 +169,14 @@ def measure(wl, args, torch, moe, marker, path=None):
         layer(u)
     torch.cuda.synchronize()
     act_per_unit = {u: int(bufs[u].n_active.cpu()[0]) for u in range(wl.units)}
+    # routed rows per expert in each unit (the load the grouped kernels see)
+    loads = np.stack([np.diff(bufs[u].offsets[:wl.E + 1].cpu().numpy()) for u in range(wl.units)])
+    top = np.sort(loads, axis=1)[:, ::-1]
+    expert_rows = {"mean_per_active_expert": round(float(loads.sum() / (loads > 0).sum()), 2),
+                   "max_mean_over_units": round(float(top[:, 0].mean()), 2),
+                   "max": int(top[:, 0].max()),
+                   "top4_mean": round(float(top[:, :4].mean()), 2),
+                   "active_experts_mean": round(float((loads > 0).sum(axis=1).mean()), 2)}
 
     # one HIP graph per step (the whole path for every layer of the step), and
     # one per step holding only the grouped-FFN calls (the dominant kernel)
@@ -289,6 +297,7 @@ def measure(wl, args, torch, moe, marker, path=None):
         "cold_ms": cold_ms, "avg_ms": avg_ms, "avg_bytes": avg_bytes, "kernel": kernel,
         "flops_per_call": flops_per_call,
         "mean_active": float(np.mean(list(act_per_unit.values()))),
+        "expert_rows": expert_rows,
         "time_launches": lambda fn, n=50: time_launches(fn, args, torch, stream, n),
     }
 
@@ -445,7 +454,8 @@ def main():
                    "layers_per_step": len(m["schedule"][0]),
                    "launch": "eager" if args.eager else "hip_graph_per_step",
                    "path": m["path"],
-                   "mean_active_experts": round(m["mean_active"], 2)},
+                   "mean_active_experts": round(m["mean_active"], 2),
+                   "expert_rows": m["expert_rows"]},
         "roofline": roofline(m),
         "cpu_baseline": None,
         "spread": m["spread"],

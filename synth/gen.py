@@ -62,6 +62,10 @@ WORKLOADS = {
     "tiny":         Workload("tiny", 1, 16, 256, 128, 8, 2, "w4a16", "none", 1),
     "decode_t2":    Workload("decode_t2", 2, 2, 2048, 768, 128, 8, "w4a16", "normal", 48),
     "prefill_t512": Workload("prefill_t512", 3, 512, 2048, 768, 128, 8, "w4a16", "normal", 48),
+    # the same prompts, weights and logit noise without the per-expert bias:
+    # the skew of prefill_t512 against uniform routing at equal T
+    "prefill_t512_flat": Workload("prefill_t512_flat", 3, 512, 2048, 768, 128, 8, "w4a16",
+                                  "none", 48),
     "w8a8_t4096":   Workload("w8a8_t4096", 4, 4096, 2048, 768, 128, 8, "w8a8", "none", 4),
     "w4a8_t512":    Workload("w4a8_t512", 7, 512, 2048, 768, 128, 8, "w4a8", "normal", 48),
     "decode_large": Workload("decode_large", 5, 2, 7168, 2048, 256, 8, "w4a16", "zipf", 16,
