@@ -21,7 +21,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kW8BM = 128;      // rows per GEMM tile (two blocks per CU; 256 measured slower)
-constexpr int kBK = 64;         // K per pipeline step (two MFMA k-steps of 32)
+constexpr int kBK = 64;         // K bytes per pipeline stage (MFMA k-steps of 32)
+constexpr int kCPR = kBK / 16;  // 16-byte chunks of a row per stage
 
 // --------------------------------------------------------- quantization ----
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
@@ -200,26 +201,43 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 // k = 32*ks + 16*hf + [0, 16).
 constexpr int kW8Stages = 3;
 constexpr int kW8BN = 256;                       // B rows per tile
-constexpr int kW8BSlots = kW8BN * 4;
+constexpr int kW8BSlots = kW8BN * kCPR;
 
-__device__ __forceinline__ int swz(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+// LDS slot of (row, chunk c) in a stage: rows of kCPR chunks, the chunk
+// index XOR-swizzled by the row so that 16 consecutive rows read at one chunk
+// fall in distinct banks (4 banks per 16-byte chunk, 64 banks)
+__device__ __forceinline__ int swz_bits(int row) { return (row / (16 / kCPR)) & (kCPR - 1); }
+__device__ __forceinline__ int swz(int row, int c) { return row * kCPR + (c ^ swz_bits(row)); }
 
 // s_waitcnt vmcnt(N) then s_barrier, for the counts the pipeline uses
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N == 0 || N == 4 || N == 6 || N == 8 || N == 12 || N == 16, "add the count here");
+  static_assert(N == 0 || N == 3 || N == 4 || N == 6 || N == 8 || N == 9 || N == 12 || N == 16,
+                "add the count here");
   if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// wait until a stage has landed while `later` later stages (of LPS loads
+// each) may still be in flight, then barrier; later <= MAXL
+template <int LPS, int MAXL>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (MAXL >= 4) { if (later >= 4) { wait_vm_barrier<4 * LPS>(); return; } }
+  if constexpr (MAXL >= 3) { if (later == 3) { wait_vm_barrier<3 * LPS>(); return; } }
+  if constexpr (MAXL >= 2) { if (later == 2) { wait_vm_barrier<2 * LPS>(); return; } }
+  if constexpr (MAXL >= 1) { if (later == 1) { wait_vm_barrier<LPS>(); return; } }
+  wait_vm_barrier<0>();
 }
 
 template <int BM>
 struct W8Geom {
   static constexpr int kThreads = BM * 2;
-  static constexpr int kASlots = BM * 4;                       // 16-byte A slots per stage
+  static constexpr int kASlots = BM * kCPR;                    // 16-byte A slots per stage
   static constexpr int kStageBytes = (kASlots + kW8BSlots) * 16;
   static constexpr int kAPer = kASlots / kThreads;              // A loads per thread per stage
   static constexpr int kBPer = kW8BSlots / kThreads;
@@ -286,13 +304,13 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
   uint32_t aoff[4], boff[4], akc[4], bkc[4];   // row offset + chunk, and the chunk's k
 #pragma unroll
   for (int v = 0; v < G::kAPer; ++v) {
-    const int s = tid + NTHR * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+    const int s = tid + NTHR * v, row = s / kCPR, c = (s % kCPR) ^ swz_bits(row);
     aoff[v] = static_cast<uint32_t>(row_src[row]) * K + c * 16;
     akc[v] = c * 16;
   }
 #pragma unroll
   for (int v = 0; v < G::kBPer; ++v) {
-    const int s = tid + NTHR * v, row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+    const int s = tid + NTHR * v, row = s / kCPR, c = (s % kCPR) ^ swz_bits(row);
     boff[v] = static_cast<uint32_t>(b_row(row)) * K + c * 16;
     bkc[v] = c * 16;
   }
@@ -333,12 +351,9 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
   for (int st = 0; st < kW8Stages - 1; ++st)
     if (st < steps) issue(st);
 
-  static_assert(kW8Stages == 3, "the waits below assume at most two stages ahead");
   for (int st = 0; st < steps; ++st) {
     // stage st is complete once at most the later in-flight stages remain
-    const int later = min(kW8Stages - 2, steps - 1 - st);
-    if (later >= 1) wait_vm_barrier<G::kLoadsPerStage>();
-    else wait_vm_barrier<0>();
+    wait_stage<G::kLoadsPerStage, kW8Stages - 2>(min(kW8Stages - 2, steps - 1 - st));
     if (st + kW8Stages - 1 < steps) issue(st + kW8Stages - 1);
     const uint8_t* base = w8_lds + (st % kW8Stages) * G::kStageBytes;
     // all operand reads of the stage first: the second k-step's reads land
