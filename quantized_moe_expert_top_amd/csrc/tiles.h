@@ -69,11 +69,13 @@ __device__ bool find_tile(const int* __restrict__ offsets, int E, int NT, int* s
   }
   __syncthreads();
   if (!mine) return false;
-  ti.e = sm_out[0];
-  ti.mt = sm_out[1];
-  ti.nt = sm_out[2];
-  ti.p_begin = sm_out[3] + ti.mt * BM;
-  ti.p_end = sm_out[4];
+  // the same for every thread of the block: kept in scalar registers, so
+  // that buffer resources built from them need no per-lane handling
+  ti.e = __builtin_amdgcn_readfirstlane(sm_out[0]);
+  ti.mt = __builtin_amdgcn_readfirstlane(sm_out[1]);
+  ti.nt = __builtin_amdgcn_readfirstlane(sm_out[2]);
+  ti.p_begin = __builtin_amdgcn_readfirstlane(sm_out[3]) + ti.mt * BM;
+  ti.p_end = __builtin_amdgcn_readfirstlane(sm_out[4]);
   return true;
 }
 

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
   constexpr int NTHR = G::kThreads;
   extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // kW8Stages * kStageBytes
   __shared__ int row_src[BM];
-  __shared__ float row_scale[BM];     // activation scale of each tile row
+  __shared__ __attribute__((aligned(16))) float row_scale[BM];  // activation scale of each tile row
   __shared__ float col_scale[kW8BN];  // weight scale of each B tile row
   __shared__ int sm_pref[NTHR / kWave];
   __shared__ int sm_out[5];
@@ -386,7 +386,8 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * 4, 0);
   }
 
-  // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4)
+  // epilogue. C layout of a 32 x 32 subtile: lane holds column l32, rows
+  // 8*(r/4) + 4*hf + (r%4).
   float cs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -394,36 +395,75 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
                                  : (wn * 128 + j * 32 + l32);
     cs[j] = col_scale[brow];
   }
+  const int mb = wm * 64 + hf * 4;   // first tile row of this lane's C rows
+  if (dbg_acc) {
+    // the raw integer accumulators, for the tests (not the timed path)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = ti.p_begin + mb + i * 32 + (r >> 2) * 8 + (r & 3);
+        if (p >= ti.p_end) continue;
+        int32_t* row = dbg_acc + static_cast<size_t>(p) * N;
+        if (KIND == 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = ti.nt * 128 + wn * 64 + j * 32 + l32;
+            if (n >= I) continue;
+            row[n] = acc[i][j][r];
+            row[I + n] = acc[i][j + 2][r];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = ti.nt * kW8BN + wn * 128 + j * 32 + l32;
+            if (n < N) row[n] = acc[i][j][r];
+          }
+        }
+      }
+  }
+  // Outputs go through a buffer resource based at the tile's first row and
+  // column, one 4-byte store per element at a 32-bit offset: rows past the
+  // expert's routed rows lie past the resource's end, and columns past the
+  // row width are sent there too, so the hardware drops both (no branch and
+  // no 64-bit address arithmetic per element).
+  const int ow = (KIND == 0) ? I : N;                      // output row width
+  const int cb = (KIND == 0) ? ti.nt * 128 : ti.nt * kW8BN;  // tile's first column
+  const int rows = min(ti.p_end - ti.p_begin, BM);
+  const uint32_t rowb = static_cast<uint32_t>(ow) * 4;
+  float* obase = ((KIND == 0) ? h_out : y_out) + static_cast<size_t>(ti.p_begin) * ow + cb;
+  const __amdgpu_buffer_rsrc_t o_rsrc =
+      buffer_rsrc(obase, static_cast<uint32_t>(rows - 1) * rowb + static_cast<uint32_t>(ow - cb) * 4);
+  constexpr int kOutCols = (KIND == 0) ? 2 : 4;
+  uint32_t coff[kOutCols];
+#pragma unroll
+  for (int j = 0; j < kOutCols; ++j) {
+    const int c = (KIND == 0) ? (wn * 64 + j * 32 + l32) : (wn * 128 + j * 32 + l32);
+    coff[j] = cb + c < ow ? static_cast<uint32_t>(mb) * rowb + c * 4 : kPastEnd;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = wm * 64 + i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-      const int p = ti.p_begin + m;
-      if (p >= ti.p_end) continue;
-      const float rs = row_scale[m];
-      if (KIND == 0) {
+    for (int q = 0; q < 4; ++q) {
+      // the four consecutive rows 8q + 4hf + [0, 4) of subtile i
+      const float4 rs4 = *reinterpret_cast<const float4*>(&row_scale[mb + i * 32 + q * 8]);
+      const float rsv[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = ti.nt * 128 + wn * 64 + j * 32 + l32;
-          if (n >= I) continue;
-          const int ag = acc[i][j][r], au = acc[i][j + 2][r];
-          if (dbg_acc) {
-            dbg_acc[static_cast<size_t>(p) * N + n] = ag;
-            dbg_acc[static_cast<size_t>(p) * N + I + n] = au;
+      for (int t = 0; t < 4; ++t) {
+        const int r = q * 4 + t;
+        const uint32_t roff = static_cast<uint32_t>(i * 32 + q * 8 + t) * rowb;
+#pragma unroll
+        for (int j = 0; j < kOutCols; ++j) {
+          float v;
+          if (KIND == 0) {
+            const float g = static_cast<float>(acc[i][j][r]) * rsv[t] * cs[j];
+            const float u = static_cast<float>(acc[i][j + 2][r]) * rsv[t] * cs[j + 2];
+            v = silu_mul(g, u);
+          } else {
+            v = static_cast<float>(acc[i][j][r]) * rsv[t] * cs[j];
           }
-          const float g = static_cast<float>(ag) * rs * cs[j];
-          const float u = static_cast<float>(au) * rs * cs[j + 2];
-          h_out[static_cast<size_t>(p) * I + n] = silu_mul(g, u);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = ti.nt * kW8BN + wn * 128 + j * 32 + l32;
-          if (n >= N) continue;
-          const int a = acc[i][j][r];
-          if (dbg_acc) dbg_acc[static_cast<size_t>(p) * N + n] = a;
-          y_out[static_cast<size_t>(p) * N + n] = static_cast<float>(a) * rs * cs[j];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), o_rsrc,
+                                                coff[j] + roff, 0, 0);
         }
       }
     }
