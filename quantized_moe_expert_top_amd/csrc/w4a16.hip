@@ -1336,25 +1336,42 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   }
 
   // epilogue: C layout of 32x32 MFMA: lane holds column l32, rows
-  // 8*(r/4) + 4*hf + (r%4), r = 0..15
+  // 8*(r/4) + 4*hf + (r%4), r = 0..15. Stores go through a buffer resource
+  // based at the tile's first row and column, at 32-bit offsets: rows past the
+  // expert's block lie past the resource's end, columns past the row width are
+  // sent there, and the hardware drops both (no branch per element).
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  constexpr uint32_t esz = (KIND == 0) ? 2 : 4;   // bf16 h or float32 y
+  const int ow = (KIND == 0) ? N / 2 : N;
+  const int cb = (KIND == 0) ? ti.nt * 128 : ti.nt * 256;
+  const int rows = min(ti.p_end - ti.p_begin, BM);
+  const uint32_t orowb = static_cast<uint32_t>(ow) * esz;
+  const __amdgpu_buffer_rsrc_t o_rsrc = buffer_rsrc(
+      static_cast<char*>(out) + (static_cast<size_t>(ti.p_begin) * ow + cb) * esz,
+      static_cast<uint32_t>(rows - 1) * orowb + static_cast<uint32_t>(ow - cb) * esz);
+  uint32_t coff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = (KIND == 0) ? wv * 32 + l32 : wv * 64 + j * 32 + l32;
+    coff[j] = nvalid[j] ? static_cast<uint32_t>(hf * 4) * orowb + c * esz : kPastEnd;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = i * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-      const int p = ti.p_begin + m;
-      if (p >= ti.p_end) continue;
+      const uint32_t roff = static_cast<uint32_t>(i * 32 + (r >> 2) * 8 + (r & 3)) * orowb;
       if (KIND == 0) {
-        if (nvalid[0]) {
-          const int n = ti.nt * 128 + wv * 32 + l32;
-          static_cast<uint16_t*>(out)[static_cast<size_t>(p) * (N / 2) + n] =
-              f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
-        }
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r])),
+                                              o_rsrc, coff[0] + roff, 0, 0);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (nvalid[j])
-            static_cast<float*>(out)[static_cast<size_t>(p) * N + nrow[j]] = acc[i][j][r];
+        for (int j = 0; j < 2; ++j) {
+          // through a scalar: a bit cast of the vector element itself read
+          // element 0 for every r (clang)
+          const float v = acc[i][j][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), o_rsrc,
+                                                coff[j] + roff, 0, 0);
+        }
       }
     }
   }

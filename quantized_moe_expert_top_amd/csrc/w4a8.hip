@@ -366,25 +366,43 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
     }
   }
 
-  // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4)
+  // epilogue; C layout: lane holds column l32, rows 8*(r/4) + 4*hf + (r%4).
+  // Stores go through a buffer resource based at the tile's first row and
+  // column, at 32-bit offsets: rows past the expert's block lie past the
+  // resource's end, columns past the row width are sent there, and the
+  // hardware drops both (no branch per element).
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  const int ow = (KIND == 0) ? N / 2 : N;
+  const int cb = (KIND == 0) ? ti.nt * 128 : ti.nt * 256;
+  const int rows = min(ti.p_end - ti.p_begin, 32 * MT);
+  const uint32_t orowb = static_cast<uint32_t>(ow) * 4;
+  const __amdgpu_buffer_rsrc_t o_rsrc =
+      buffer_rsrc(out + static_cast<size_t>(ti.p_begin) * ow + cb,
+                  static_cast<uint32_t>(rows - 1) * orowb + static_cast<uint32_t>(ow - cb) * 4);
+  uint32_t coff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = (KIND == 0) ? wv * 32 + l32 : wv * 64 + j * 32 + l32;
+    coff[j] = nvalid[j] ? static_cast<uint32_t>(hf * 4) * orowb + c * 4 : kPastEnd;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 32 * i + (r >> 2) * 8 + hf * 4 + (r & 3);
-      const int p = ti.p_begin + m;
-      if (p >= ti.p_end) continue;
+      const uint32_t roff = static_cast<uint32_t>(m - hf * 4) * orowb;
       const float rs = row_scale[m] * 0.0625f;   // the operand codes carry a factor 16
       if (KIND == 0) {
-        if (nvalid[0]) {
-          const int n = ti.nt * 128 + wv * 32 + l32;
-          out[static_cast<size_t>(p) * (N / 2) + n] =
-              silu_mul(acc[i][0][r] * rs, acc[i][1][r] * rs);
-        }
+        const float v = silu_mul(acc[i][0][r] * rs, acc[i][1][r] * rs);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), o_rsrc,
+                                              coff[0] + roff, 0, 0);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (nvalid[j]) out[static_cast<size_t>(p) * N + nrow[j]] = acc[i][j][r] * rs;
+        for (int j = 0; j < 2; ++j) {
+          const float v = acc[i][j][r] * rs;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), o_rsrc,
+                                                coff[j] + roff, 0, 0);
+        }
       }
     }
 }

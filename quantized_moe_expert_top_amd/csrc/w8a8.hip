@@ -20,9 +20,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kW8BM = 128;      // rows per GEMM tile (two blocks per CU; 256 measured slower)
-constexpr int kBK = 64;         // K bytes per pipeline stage (MFMA k-steps of 32)
-constexpr int kCPR = kBK / 16;  // 16-byte chunks of a row per stage
 
 // --------------------------------------------------------- quantization ----
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
@@ -175,23 +172,21 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------- int8 GEMM ----
-// A block has BM/64 x 2 waves (BM * 2 threads); each wave owns 64 tile rows
-// and 128 B rows (two 32-row by four 32-column MFMA subtiles).
+// Tiles of BM rows x 256 B rows. A block has WM x WN waves; wave (wm, wn) owns
+// BM/WM tile rows and 256/WN B rows as 32 x 32 MFMA subtiles (MI x NJ).
 // KIND 0: gate/up. Tile = BM rows x 128 h-columns: the B tile holds the 128
-//         gate rows and the 128 matching up rows (256 W13 rows). Wave (wm, wn)
-//         owns rows [64wm, +64) and h-columns [64wn, +64): subtiles 0,1
-//         gate, 2,3 the matching up rows. Out: h float32 [R, I].
-// KIND 1: down. Tile = BM rows x 256 W2 rows; wave (wm, wn) owns rows
-//         [64wm, +64) and W2 rows [128wn, +128) as four subtiles. Out: y.
-// BM = 128: 256 threads, two blocks per CU. BM = 256: 512 threads, one block
-// per CU, each B strip staged once for twice the rows.
-// Pipeline: K advances in 64-byte stages; kW8Stages stages are in flight,
+//         gate rows and the 128 matching up rows (256 W13 rows). Wave wn owns
+//         h-columns [wn*128/WN, +128/WN): its first NJ/2 subtiles are those
+//         gate rows, the last NJ/2 the matching up rows. Out: h float32 [R, I].
+// KIND 1: down. Tile = BM rows x 256 W2 rows; wave wn owns W2 rows
+//         [wn*256/WN, +256/WN). Out: y float32 [R, H].
+// Pipeline: K advances in BK-byte stages; kStages stages rotate through LDS,
 // each moved HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging;
 // the buffer form, unlike the global one, leaves LDS reads countable in order,
-// so operand reads overlap the MFMAs). A wave
-// instruction fills 64 consecutive 16-byte LDS slots; slot s of a tile holds
-// row s/4, chunk (s%4) ^ ((row/4)%4), so each row's 64 bytes are still read as
-// one coalesced run while the MFMA operand reads (32 rows, one chunk each) hit
+// so operand reads overlap the MFMAs). A wave instruction fills 64
+// consecutive 16-byte LDS slots; slot s of a tile holds row s/CPR, chunk
+// (s%CPR) ^ swizzle(row), so each row's BK bytes are still read as one
+// coalesced run while the MFMA operand reads (32 rows, one chunk each) hit
 // distinct LDS banks. Waits are explicit (vmcnt + barrier) so loads of later
 // stages stay in flight across the barrier: each stage is exactly
 // kLoadsPerStage vector-memory instructions per thread and nothing else in
@@ -199,15 +194,43 @@ __global__ __launch_bounds__(kThreads) void h_quant_kernel(const float* __restri
 // spills to scratch, which would add such instructions).
 // MFMA operand k order inside one 32-k step: lane half hf = lane/32 takes
 // k = 32*ks + 16*hf + [0, 16).
-constexpr int kW8Stages = 3;
 constexpr int kW8BN = 256;                       // B rows per tile
-constexpr int kW8BSlots = kW8BN * kCPR;
 
-// LDS slot of (row, chunk c) in a stage: rows of kCPR chunks, the chunk
-// index XOR-swizzled by the row so that 16 consecutive rows read at one chunk
-// fall in distinct banks (4 banks per 16-byte chunk, 64 banks)
-__device__ __forceinline__ int swz_bits(int row) { return (row / (16 / kCPR)) & (kCPR - 1); }
-__device__ __forceinline__ int swz(int row, int c) { return row * kCPR + (c ^ swz_bits(row)); }
+template <int BM_, int WM_, int WN_, int BK_, int STAGES_, int BPC_>
+struct W8Geom {
+  static constexpr int BM = BM_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int kStages = STAGES_;
+  static constexpr int kThreads = WM * WN * kWave;
+  static constexpr int kCPR = BK / 16;                          // 16-byte chunks of a row per stage
+  static constexpr int kMI = BM / WM / 32;                      // 32-row subtiles per wave
+  static constexpr int kNJ = kW8BN / WN / 32;                   // 32-column subtiles per wave
+  static constexpr int kASlots = BM * kCPR;                     // 16-byte A slots per stage
+  static constexpr int kBSlots = kW8BN * kCPR;
+  static constexpr int kStageBytes = (kASlots + kBSlots) * 16;
+  static constexpr int kAPer = kASlots / kThreads;              // A loads per thread per stage
+  static constexpr int kBPer = kBSlots / kThreads;
+  static constexpr int kLoadsPerStage = kAPer + kBPer;
+  static constexpr int kBlocksPerCU = BPC_;
+  static_assert(kASlots % kThreads == 0 && kBSlots % kThreads == 0, "slots split evenly");
+  static_assert(kMI >= 1 && kNJ >= 2 && kNJ % 2 == 0 && kNJ <= 4, "wave tile shape");
+  static_assert(kAPer <= 8 && kBPer <= 8, "slot arrays hold eight per thread");
+  // dynamic stages plus about 4 KB of static arrays per block
+  static_assert(kBlocksPerCU * (kStages * kStageBytes + 4096) <= 160 * 1024, "LDS per CU");
+};
+// four waves, 64-byte stages, two blocks per CU. Measured against it at
+// T 4096 (same box): eight waves with 128-byte stages at one block per CU
+// (each row's stage one whole cache line) ran the FFN 4% slower, and the same
+// with stages staged through registers (three or four in flight per thread)
+// 12% and 40% slower.
+using W8Tile = W8Geom<128, 2, 2, 64, 3, 2>;
+
+// LDS slot of (row, chunk c) in a stage: rows of CPR chunks, the chunk index
+// XOR-swizzled by the row so that 16 consecutive rows read at one chunk fall
+// in distinct banks (4 banks per 16-byte chunk, 64 banks)
+template <int CPR>
+__device__ __forceinline__ int swz_bits(int row) { return (row / (16 / CPR)) & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) { return row * CPR + (c ^ swz_bits<CPR>(row)); }
 
 // s_waitcnt vmcnt(N) then s_barrier, for the counts the pipeline uses
 template <int N>
@@ -234,29 +257,19 @@ __device__ __forceinline__ void wait_stage(int later) {
   wait_vm_barrier<0>();
 }
 
-template <int BM>
-struct W8Geom {
-  static constexpr int kThreads = BM * 2;
-  static constexpr int kASlots = BM * kCPR;                    // 16-byte A slots per stage
-  static constexpr int kStageBytes = (kASlots + kW8BSlots) * 16;
-  static constexpr int kAPer = kASlots / kThreads;              // A loads per thread per stage
-  static constexpr int kBPer = kW8BSlots / kThreads;
-  static constexpr int kLoadsPerStage = kAPer + kBPer;
-  static constexpr int kMI = 2;                                 // 32-row subtiles per wave
-  static constexpr int kBlocksPerCU = BM == 128 ? 2 : 1;
-};
-
-template <int KIND, int BM>
-__global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) void w8a8_mfma_kernel(
+template <int KIND, class G>
+__global__ __launch_bounds__(G::kThreads, G::kBlocksPerCU) void w8a8_mfma_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const int8_t* __restrict__ W, const float* __restrict__ w_scale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_slot, int a_rows, int K,
     int N, int E, int topk, int NT, float* __restrict__ h_out, float* __restrict__ y_out,
     int32_t* __restrict__ dbg_acc) {
-  using G = W8Geom<BM>;
-  constexpr int MI = G::kMI;
-  constexpr int NTHR = G::kThreads;
-  extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // kW8Stages * kStageBytes
+  constexpr int BM = G::BM, MI = G::kMI, NJ = G::kNJ, NTHR = G::kThreads;
+  constexpr int BK = G::BK, CPR = G::kCPR, STAGES = G::kStages;
+  constexpr int RW = BM / G::WM;        // tile rows per wave
+  constexpr int HCW = 128 / G::WN;      // h-columns per wave (gate/up)
+  constexpr int BW = kW8BN / G::WN;     // B rows per wave (down)
+  extern __shared__ __attribute__((aligned(16))) uint8_t w8_lds[];  // STAGES * kStageBytes
   __shared__ int row_src[BM];
   __shared__ __attribute__((aligned(16))) float row_scale[BM];  // activation scale of each tile row
   __shared__ float col_scale[kW8BN];  // weight scale of each B tile row
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int wm = wv >> 1, wn = wv & 1;   // wave's 64-row band and B half
+  const int wm = wv / G::WN, wn = wv % G::WN;   // wave's row band and B band
   const int I = N / 2;  // KIND 0 only
 
   // W row held at B tile row j (0..255)
@@ -280,6 +293,11 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
     const int r = ti.nt * kW8BN + j;
     return r < N ? r : N - 1;
   };
+  // B tile row of this lane in the wave's subtile j
+  auto b_tile_row = [&](int j) -> int {
+    if (KIND == 0) return (j / (NJ / 2)) * 128 + wn * HCW + (j % (NJ / 2)) * 32 + l32;
+    return wn * BW + j * 32 + l32;
+  };
   // source row of each A tile row (token for gate/up, grouped row for down);
   // rows past the expert's block read the tile's first row (results dropped).
   // The scales the epilogue needs are staged here, off its critical path.
@@ -290,7 +308,8 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
     row_src[r] = src;
     row_scale[r] = a_scale[src];
   }
-  if (tid < kW8BN) col_scale[tid] = w_scale[static_cast<size_t>(ti.e) * N + b_row(tid)];
+  for (int j = tid; j < kW8BN; j += NTHR)
+    col_scale[j] = w_scale[static_cast<size_t>(ti.e) * N + b_row(j)];
   __syncthreads();
 
   // this thread's A and B slots per stage (slot = wave * 64 + lane + NTHR * v),
@@ -300,29 +319,28 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * K, static_cast<uint32_t>(N) * K);
   // fixed-size arrays: a lambda capturing arrays whose size depends on the
   // template parameters makes the host pass drop the kernel's launch stub
-  static_assert(G::kAPer <= 4 && G::kBPer <= 4, "slot arrays hold four per thread");
-  uint32_t aoff[4], boff[4], akc[4], bkc[4];   // row offset + chunk, and the chunk's k
+  uint32_t aoff[8], boff[8], akc[8], bkc[8];   // row offset + chunk, and the chunk's k
 #pragma unroll
   for (int v = 0; v < G::kAPer; ++v) {
-    const int s = tid + NTHR * v, row = s / kCPR, c = (s % kCPR) ^ swz_bits(row);
+    const int s = tid + NTHR * v, row = s / CPR, c = (s % CPR) ^ swz_bits<CPR>(row);
     aoff[v] = static_cast<uint32_t>(row_src[row]) * K + c * 16;
     akc[v] = c * 16;
   }
 #pragma unroll
   for (int v = 0; v < G::kBPer; ++v) {
-    const int s = tid + NTHR * v, row = s / kCPR, c = (s % kCPR) ^ swz_bits(row);
+    const int s = tid + NTHR * v, row = s / CPR, c = (s % CPR) ^ swz_bits<CPR>(row);
     boff[v] = static_cast<uint32_t>(b_row(row)) * K + c * 16;
     bkc[v] = c * 16;
   }
-  // K % 64 may be 16, 32 or 48: the last stage's chunks past K read at an
-  // offset past the buffer's end, which the hardware returns as zeros (an
+  // K % BK may be any multiple of 16: the last stage's chunks past K read at
+  // an offset past the buffer's end, which the hardware returns as zeros (an
   // exact zero term in every dot product)
   constexpr uint32_t kPastEnd = 0x80000000u;   // beyond any buffer resource here
   const uint32_t Ku = static_cast<uint32_t>(K);
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   auto issue = [&](int st) {
-    uint8_t* base = w8_lds + (st % kW8Stages) * G::kStageBytes + wvu * kWave * 16;
-    const uint32_t k0 = static_cast<uint32_t>(st) * kBK;
+    uint8_t* base = w8_lds + (st % STAGES) * G::kStageBytes + wvu * kWave * 16;
+    const uint32_t k0 = static_cast<uint32_t>(st) * BK;
 #pragma unroll
     for (int v = 0; v < G::kAPer; ++v)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -335,67 +353,65 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
           k0 + bkc[v] < Ku ? boff[v] + k0 : kPastEnd, 0, 0, 0);
   };
 
-  i32x16_t acc[MI][4];
+  // fixed size (see the slot arrays above); MI x NJ of it is used
+  static_assert(MI <= 2 && NJ <= 4, "accumulator array holds 2 x 4 subtiles");
+  i32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  const int steps = (K + kBK - 1) / kBK;
+  const int steps = (K + BK - 1) / BK;
   // land the epilogue's kernel arguments now: a scalar load still in flight
   // inside the loop would turn every LDS wait there into a full drain
   asm volatile("" ::"s"(h_out), "s"(y_out), "s"(dbg_acc));
+  // the stage's LDS reads, then its MFMAs
+  auto compute = [&](const uint8_t* base) {
+    i32x4_t aop[BK / 32][MI], bop[BK / 32][NJ];
 #pragma unroll
-  for (int st = 0; st < kW8Stages - 1; ++st)
-    if (st < steps) issue(st);
-
-  for (int st = 0; st < steps; ++st) {
-    // stage st is complete once at most the later in-flight stages remain
-    wait_stage<G::kLoadsPerStage, kW8Stages - 2>(min(kW8Stages - 2, steps - 1 - st));
-    if (st + kW8Stages - 1 < steps) issue(st + kW8Stages - 1);
-    const uint8_t* base = w8_lds + (st % kW8Stages) * G::kStageBytes;
-    // all operand reads of the stage first: the second k-step's reads land
-    // while the first k-step's MFMAs run
-    i32x4_t aop[kBK / 32][MI], bop[kBK / 32][4];
-#pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
+    for (int ks = 0; ks < BK / 32; ++ks) {
       const int c = 2 * ks + hf;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int arow = wm * 64 + i * 32 + l32;
-        aop[ks][i] = *reinterpret_cast<const i32x4_t*>(base + swz(arow, c) * 16);
+        const int arow = wm * RW + i * 32 + l32;
+        aop[ks][i] = *reinterpret_cast<const i32x4_t*>(base + swz<CPR>(arow, c) * 16);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int brow = (KIND == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32)
-                                     : (wn * 128 + j * 32 + l32);
-        bop[ks][j] = *reinterpret_cast<const i32x4_t*>(base + (G::kASlots + swz(brow, c)) * 16);
-      }
+      for (int j = 0; j < NJ; ++j)
+        bop[ks][j] = *reinterpret_cast<const i32x4_t*>(
+            base + (G::kASlots + swz<CPR>(b_tile_row(j), c)) * 16);
     }
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks)
+    for (int ks = 0; ks < BK / 32; ++ks)
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[ks][i], bop[ks][j], acc[i][j], 0, 0, 0);
-    // keep that order through scheduling: the stage's LDS reads, then its MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + 4), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI * 4, 0);
+    // keep that order through scheduling: later k-steps' reads land while the
+    // first k-step's MFMAs run
+    __builtin_amdgcn_sched_group_barrier(0x100, (BK / 32) * (MI + NJ), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, (BK / 32) * MI * NJ, 0);
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < steps) issue(st);
+  for (int st = 0; st < steps; ++st) {
+    // stage st is complete once at most the later in-flight stages remain
+    wait_stage<G::kLoadsPerStage, STAGES - 2>(min(STAGES - 2, steps - 1 - st));
+    if (st + STAGES - 1 < steps) issue(st + STAGES - 1);
+    compute(w8_lds + (st % STAGES) * G::kStageBytes);
   }
 
   // epilogue. C layout of a 32 x 32 subtile: lane holds column l32, rows
   // 8*(r/4) + 4*hf + (r%4).
-  float cs[4];
+  float cs[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int brow = (KIND == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + l32)
-                                 : (wn * 128 + j * 32 + l32);
-    cs[j] = col_scale[brow];
-  }
-  const int mb = wm * 64 + hf * 4;   // first tile row of this lane's C rows
+  for (int j = 0; j < NJ; ++j) cs[j] = col_scale[b_tile_row(j)];
+  const int mb = wm * RW + hf * 4;   // first tile row of this lane's C rows
   if (dbg_acc) {
     // the raw integer accumulators, for the tests (not the timed path)
 #pragma unroll
@@ -407,16 +423,16 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
         int32_t* row = dbg_acc + static_cast<size_t>(p) * N;
         if (KIND == 0) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int n = ti.nt * 128 + wn * 64 + j * 32 + l32;
+          for (int j = 0; j < NJ / 2; ++j) {
+            const int n = ti.nt * 128 + wn * HCW + j * 32 + l32;
             if (n >= I) continue;
             row[n] = acc[i][j][r];
-            row[I + n] = acc[i][j + 2][r];
+            row[I + n] = acc[i][j + NJ / 2][r];
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = ti.nt * kW8BN + wn * 128 + j * 32 + l32;
+          for (int j = 0; j < NJ; ++j) {
+            const int n = ti.nt * kW8BN + wn * BW + j * 32 + l32;
             if (n < N) row[n] = acc[i][j][r];
           }
         }
@@ -427,18 +443,18 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
   // expert's routed rows lie past the resource's end, and columns past the
   // row width are sent there too, so the hardware drops both (no branch and
   // no 64-bit address arithmetic per element).
-  const int ow = (KIND == 0) ? I : N;                      // output row width
+  const int ow = (KIND == 0) ? I : N;                        // output row width
   const int cb = (KIND == 0) ? ti.nt * 128 : ti.nt * kW8BN;  // tile's first column
   const int rows = min(ti.p_end - ti.p_begin, BM);
   const uint32_t rowb = static_cast<uint32_t>(ow) * 4;
   float* obase = ((KIND == 0) ? h_out : y_out) + static_cast<size_t>(ti.p_begin) * ow + cb;
   const __amdgpu_buffer_rsrc_t o_rsrc =
       buffer_rsrc(obase, static_cast<uint32_t>(rows - 1) * rowb + static_cast<uint32_t>(ow - cb) * 4);
-  constexpr int kOutCols = (KIND == 0) ? 2 : 4;
+  constexpr int kOutCols = (KIND == 0) ? NJ / 2 : NJ;
   uint32_t coff[kOutCols];
 #pragma unroll
   for (int j = 0; j < kOutCols; ++j) {
-    const int c = (KIND == 0) ? (wn * 64 + j * 32 + l32) : (wn * 128 + j * 32 + l32);
+    const int c = (KIND == 0) ? (wn * HCW + j * 32 + l32) : (wn * BW + j * 32 + l32);
     coff[j] = cb + c < ow ? static_cast<uint32_t>(mb) * rowb + c * 4 : kPastEnd;
   }
 #pragma unroll
@@ -457,7 +473,7 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
           float v;
           if (KIND == 0) {
             const float g = static_cast<float>(acc[i][j][r]) * rsv[t] * cs[j];
-            const float u = static_cast<float>(acc[i][j + 2][r]) * rsv[t] * cs[j + 2];
+            const float u = static_cast<float>(acc[i][j + NJ / 2][r]) * rsv[t] * cs[j + NJ / 2];
             v = silu_mul(g, u);
           } else {
             v = static_cast<float>(acc[i][j][r]) * rsv[t] * cs[j];
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(W8Geom<BM>::kThreads, W8Geom<BM>::kBlocksPerCU) voi
   }
 }
 
-template <int KIND, int BM>
+template <int KIND, class G>
 hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t* W,
                             const float* w_scale, const int* offsets, const int* sorted_slot,
                             int K, int N, int E, int topk, int T, float* h_out, float* y_out,
@@ -478,15 +494,15 @@ hipError_t launch_w8a8_gemm(const int8_t* A, const float* a_scale, const int8_t*
   const int NT = (KIND == 0) ? (N / 2 + 127) / 128 : (N + kW8BN - 1) / kW8BN;
   const long long R = static_cast<long long>(T) * topk;
   const long long act = R < E ? R : E;
-  const long long mt_up = (R + BM - 1) / BM + act;
+  const long long mt_up = (R + G::BM - 1) / G::BM + act;
   long long grid = (mt_up * NT + 7) / 8 * 8;
-  const size_t lds = static_cast<size_t>(kW8Stages) * W8Geom<BM>::kStageBytes;
+  const size_t lds = static_cast<size_t>(G::kStages) * G::kStageBytes;
   const hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w8a8_mfma_kernel<KIND, BM>),
+      reinterpret_cast<const void*>(&w8a8_mfma_kernel<KIND, G>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((w8a8_mfma_kernel<KIND, BM>), dim3(static_cast<unsigned>(grid)),
-                     dim3(W8Geom<BM>::kThreads), lds, s, A, a_scale, W, w_scale, offsets, sorted_slot,
+  hipLaunchKernelGGL((w8a8_mfma_kernel<KIND, G>), dim3(static_cast<unsigned>(grid)),
+                     dim3(G::kThreads), lds, s, A, a_scale, W, w_scale, offsets, sorted_slot,
                      static_cast<int>(KIND == 0 ? T : R), K, N, E, topk, NT, h_out, y_out, dbg_acc);
   return hipGetLastError();
 }
@@ -536,14 +552,14 @@ hipError_t launch_w8a8_ffn(int T, int H, int I, int E, int k, const uint16_t* x,
       x, T, H, w.xq, w.xs, dbg.xq, dbg.xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_w8a8_gemm<0, kW8BM>(w.xq, w.xs, w13, s13, offsets, sorted_slot, H, 2 * I, E, k, T,
+  err = launch_w8a8_gemm<0, W8Tile>(w.xq, w.xs, w13, s13, offsets, sorted_slot, H, 2 * I, E, k, T,
                                    w.h, nullptr, dbg.acc13, s);
   if (err != hipSuccess) return err;
   h_quant_kernel<<<(R + rows_per_block - 1) / rows_per_block, kThreads, 0, s>>>(
       w.h, R, I, w.hq, w.hs, dbg.hq, dbg.hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_w8a8_gemm<1, kW8BM>(w.hq, w.hs, w2, s2, offsets, sorted_slot, I, H, E, k, T,
+  return launch_w8a8_gemm<1, W8Tile>(w.hq, w.hs, w2, s2, offsets, sorted_slot, I, H, E, k, T,
                                     nullptr, y, dbg.acc2, s);
 }
 
