@@ -1105,9 +1105,10 @@ struct DecodeDownLaunch {
 // KIND 1: down. Wave w owns W2 rows [nt*256 + 64w, +64) as two subtiles.
 // K advances one scale group (128 k) per step with kMfD groups in flight:
 // each step requests group g + kMfD - 1 into a register ring of kMfD groups
-// per lane (the B codes and raw fp16 scales, and this thread's share of the
-// activation tile), computes group g, then writes group g + 1's activations,
-// pair-permuted, into its LDS stage. The LDS tile slot L of a stage holds row
+// per lane (the B codes, 64 contiguous bytes a row, and this thread's share of
+// the activation tile), computes group g, then writes group g + 1's
+// activations, pair-permuted, into its LDS stage. Computing a group starts by
+// moving its codes through the wave's own LDS area into the operand layout. The LDS tile slot L of a stage holds row
 // L/16, 16-byte chunk (L%16) ^ (row%16), so the 32 rows an MFMA operand read
 // touches land in distinct banks.
 // Operand k order: within each 16-k MFMA step s, lane half hf = lane/32 takes
@@ -1128,6 +1129,8 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   constexpr int CPT = BM * 16 / kThreads;   // activation chunks per thread per group
   constexpr int STAGE = BM * 16 * 16;       // bytes of one activation stage
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kMfD * STAGE];
+  // per wave: one group's codes of its two 32-row B subtiles (64 bytes a row)
+  __shared__ __attribute__((aligned(16))) uint8_t b_lds[kThreads / kWave][2 * 32 * 64];
   __shared__ int row_src[BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[5];
@@ -1170,31 +1173,32 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
     row_src[tid] = (KIND == 0) ? sorted_slot[pv] / topk : pv;
   }
 
-  // B rows of this lane (two subtiles)
-  int nrow[2];
+  // whether this lane's B columns exist (two subtiles)
   bool nvalid[2];
   if (KIND == 0) {
     const int n = ti.nt * 128 + wv * 32 + l32;  // h column
     nvalid[0] = nvalid[1] = n < N / 2;
-    const int nc = nvalid[0] ? n : N / 2 - 1;
-    nrow[0] = nc;
-    nrow[1] = N / 2 + nc;
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = ti.nt * 256 + wv * 64 + j * 32 + l32;
-      nvalid[j] = n < N;
-      nrow[j] = nvalid[j] ? n : N - 1;
-    }
+    for (int j = 0; j < 2; ++j) nvalid[j] = ti.nt * 256 + wv * 64 + j * 32 + l32 < N;
   }
   // codes and scales of this expert through buffer resources: per-lane row
   // offsets stay fixed, the group advances a scalar offset
   const uint32_t rowb = static_cast<uint32_t>(K / 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * rowb, static_cast<uint32_t>(N) * rowb);
+  // Codes are fetched row-contiguous: a wave instruction reads 16 rows x 64
+  // bytes (four lanes a row, one 16-byte chunk each), rows 0-15 of a subtile
+  // in one load and rows 16-31 in the next. Compute moves them through the
+  // wave's LDS area into the MFMA operand layout. Rows past the expert read
+  // as zeros (or as the up rows, for a gate tile past I); their columns are
+  // dropped.
   uint32_t woff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
+  for (int j = 0; j < 2; ++j) {
+    const int row0 = (KIND == 0) ? j * (N / 2) + ti.nt * 128 + wv * 32 : ti.nt * 256 + wv * 64 + j * 32;
+    woff[j] = static_cast<uint32_t>(row0 + (lane >> 2)) * rowb + (lane & 3) * 16;
+  }
   // this lane's rows within the tile's 256 scale rows
   int srow[2];
 #pragma unroll
@@ -1242,7 +1246,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
       b.q[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 w_rsrc, woff[j], g * 64, 0));
       b.q[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                w_rsrc, woff[j] + 16, g * 64, 0));
+                                                w_rsrc, woff[j] + 16 * rowb, g * 64, 0));
     }
 #pragma unroll
     for (int v = 0; v < CPT; ++v) b.a[v] = ld16(asrc[v] + g * kGroup);
@@ -1266,6 +1270,27 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   const NibbleConsts nk = nibble_consts();
   auto compute = [&](const Grp& b, int stage, int g) {
     const uint8_t* st = a_lds + stage * STAGE;
+    // the group's codes into the operand layout: lane (l32, hf) takes bytes
+    // [32 hf, +32) of row l32. Slot (row, chunk c) sits at row * 4 +
+    // (c ^ (row / 4 % 4)), so both the writes (16 rows x 4 chunks) and the
+    // reads (32 rows, one chunk each) hit distinct banks. The wave's LDS
+    // operations complete in order, so no wait or barrier is needed.
+    uint8_t* bw = b_lds[wv];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = h * 16 + (lane >> 2), c = lane & 3;
+        *reinterpret_cast<uint4*>(bw + j * 2048 + (row * 4 + (c ^ ((row >> 2) & 3))) * 16) = b.q[j][h];
+      }
+    uint4 bq[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = 2 * hf + t;
+        bq[j][t] = *reinterpret_cast<const uint4*>(bw + j * 2048 + (l32 * 4 + (c ^ ((l32 >> 2) & 3))) * 16);
+      }
     f32x16_t accg[MT][2], cg[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -1291,7 +1316,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
       bf16x8_t bop[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t w = (&b.q[j][s >> 2].x)[s & 3];
+        const uint32_t w = (&bq[j][s >> 2].x)[s & 3];
         uint4 pq;
         nibble_pairs_r(w, nk, pq.x, pq.y, pq.z, pq.w);
         bop[j] = __builtin_bit_cast(bf16x8_t, pq);

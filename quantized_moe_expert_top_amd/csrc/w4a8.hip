@@ -151,6 +151,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
   constexpr int BM = 32 * MT;        // tile rows: MT m-subtiles of 32 share each B fragment
   constexpr int STAGE = BM * 128;    // bytes of one activation stage
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * STAGE];
+  // per wave: one group's codes of its two 32-row B subtiles (64 bytes a row)
+  __shared__ __attribute__((aligned(16))) uint8_t b_lds[kThreads / kWave][2 * 32 * 64];
   __shared__ int row_src[BM];
   __shared__ float row_scale[BM];
   __shared__ int sm_pref[kThreads / kWave];
@@ -164,30 +166,32 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
   const int l32 = lane & 31, hf = lane >> 5;
   const int G = K / kGroup;
 
-  int nrow[2];
+  // whether this lane's B columns exist (two subtiles)
   bool nvalid[2];
   if (KIND == 0) {
-    const int n = ti.nt * 128 + wv * 32 + l32;
+    const int n = ti.nt * 128 + wv * 32 + l32;  // h column
     nvalid[0] = nvalid[1] = n < N / 2;
-    const int nc = nvalid[0] ? n : N / 2 - 1;
-    nrow[0] = nc;
-    nrow[1] = N / 2 + nc;
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = ti.nt * 256 + wv * 64 + j * 32 + l32;
-      nvalid[j] = n < N;
-      nrow[j] = nvalid[j] ? n : N - 1;
-    }
+    for (int j = 0; j < 2; ++j) nvalid[j] = ti.nt * 256 + wv * 64 + j * 32 + l32 < N;
   }
   const uint32_t rowb = static_cast<uint32_t>(K / 2);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       buffer_rsrc(W + static_cast<size_t>(ti.e) * N * rowb, static_cast<uint32_t>(N) * rowb);
   const __amdgpu_buffer_rsrc_t s_rsrc =
       buffer_rsrc(S + static_cast<size_t>(ti.e) * N * G, static_cast<uint32_t>(N * G) * 2u);
+  // Codes are fetched row-contiguous: a wave instruction reads 16 rows x 64
+  // bytes (four lanes a row, one 16-byte chunk each), rows 0-15 of a subtile
+  // in one load and rows 16-31 in the next. Compute moves them through the
+  // wave's LDS area into the MFMA operand layout. Rows past the expert read
+  // as zeros (or as the up rows, for a gate tile past I); their columns are
+  // dropped.
   uint32_t woff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) woff[j] = static_cast<uint32_t>(nrow[j]) * rowb + hf * 32;
+  for (int j = 0; j < 2; ++j) {
+    const int row0 = (KIND == 0) ? j * (N / 2) + ti.nt * 128 + wv * 32 : ti.nt * 256 + wv * 64 + j * 32;
+    woff[j] = static_cast<uint32_t>(row0 + (lane >> 2)) * rowb + (lane & 3) * 16;
+  }
   // this lane's rows within the tile's 256 scale rows
   int srow[2];
 #pragma unroll
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
       b.q[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 w_rsrc, woff[j], g * 64, 0));
       b.q[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                w_rsrc, woff[j] + 16, g * 64, 0));
+                                                w_rsrc, woff[j] + 16 * rowb, g * 64, 0));
     }
   };
   // the weight strip does not depend on the rows: start streaming it first
@@ -292,6 +296,27 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
   };
   auto compute = [&](const Grp& b, int stage, int g) {
     const uint8_t* st = a_lds + stage * STAGE;
+    // the group's codes into the operand layout: lane (l32, hf) takes bytes
+    // [32 hf, +32) of row l32. Slot (row, chunk c) sits at row * 4 +
+    // (c ^ (row / 4 % 4)), so both the writes (16 rows x 4 chunks) and the
+    // reads (32 rows, one chunk each) hit distinct banks. The wave's LDS
+    // operations complete in order, so no wait or barrier is needed.
+    uint8_t* bw = b_lds[wv];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = h * 16 + (lane >> 2), c = lane & 3;
+        *reinterpret_cast<uint4*>(bw + j * 2048 + (row * 4 + (c ^ ((row >> 2) & 3))) * 16) = b.q[j][h];
+      }
+    uint4 bq[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = 2 * hf + t;
+        bq[j][t] = *reinterpret_cast<const uint4*>(bw + j * 2048 + (l32 * 4 + (c ^ ((l32 >> 2) & 3))) * 16);
+      }
     uint4 av[MT][4];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -314,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // step s uses bytes [8s, 8s + 8) of the lane's 32 code bytes
-        const uint32_t w0 = (&b.q[j][s >> 1].x)[(s & 1) * 2];
-        const uint32_t w1 = (&b.q[j][s >> 1].x)[(s & 1) * 2 + 1];
+        const uint32_t w0 = (&bq[j][s >> 1].x)[(s & 1) * 2];
+        const uint32_t w1 = (&bq[j][s >> 1].x)[(s & 1) * 2 + 1];
         uint32_t e0, o0, e1, o1;
         unpack(w0, e0, o0);
         unpack(w1, e1, o1);
