@@ -107,3 +107,33 @@ def test_built_objects_came_with_no_spills():
     assert os.path.exists(obj)
     assert any("w8a8_mfma_kernel" in k for k in res)
     assert build.spilling(res) == {}
+
+
+def test_trace_summary_counts_only_the_marked_range(tmp_path):
+    """trace_summary keeps the dispatches that start inside the named roctx
+    range (the timed graph replays) and drops the rest (eager pass, warmup)."""
+    import sqlite3
+    import trace_summary
+    db = tmp_path / "kt_results.db"
+    con = sqlite3.connect(db)
+    con.execute("create table regions (start integer, end integer, extdata text)")
+    con.execute("create table kernels (name text, start integer, duration integer)")
+    con.execute("insert into regions values (1000, 2000, ?)", (json.dumps({"message": "timed_steps w"}),))
+    con.execute("insert into regions values (3000, 4000, ?)", (json.dumps({"message": "timed_ffn w"}),))
+    rows = [
+        ("void moe::(anonymous namespace)::a_kernel<1>(int*)", 500, 70),   # before: warmup
+        ("void moe::(anonymous namespace)::a_kernel<1>(int*)", 1100, 10),
+        ("void moe::(anonymous namespace)::b_kernel(float*)", 1200, 30),
+        ("void moe::(anonymous namespace)::a_kernel<1>(int*)", 1900, 20),
+        ("void moe::(anonymous namespace)::b_kernel(float*)", 3500, 99),   # other range
+    ]
+    con.executemany("insert into kernels values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    s = trace_summary.summarize(str(db), "timed_steps w", 2)
+    got = {name: (calls, avg, tot) for name, calls, avg, tot in s["rows"]}
+    assert got == {"a_kernel<1>": (2, 15.0, 30), "b_kernel": (1, 30.0, 30)}
+    assert s["kernel_ns"] == 60 and s["region_ns"] == 1000
+    assert "| `b_kernel` | 1 | 0.03 | 0.0 | 50.0% |" in trace_summary.markdown(s)
+    with pytest.raises(SystemExit):
+        trace_summary.summarize(str(db), "no such range", 1)
