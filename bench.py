@@ -420,7 +420,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the layer path runs on a single GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     import quantized_moe_expert_top_amd as moe
