@@ -516,6 +516,36 @@ def test_layer_entry_matches_oracle_and_calls(case):
     np.testing.assert_array_equal(got["out_bits"], calls["out_bits"])
 
 
+def _layer_sweep_cases(n=10, seed=2027):
+    """Seeded random decode shapes for the whole-layer entry (T <= 4, the fused
+    kernels): H up to 3072 and I from 256 in steps of 128, E from 1 to 300,
+    k up to min(E, 16); slot-per-block and persistent gate/up and every lane
+    split they pick. I >= 256 for the reason given at _sweep_cases."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 5))
+        H = 128 * int(rng.integers(1, 25))
+        I = 128 * int(rng.integers(2, 9))
+        E = int(rng.integers(1, 301))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        out.append((f"lsweep{i}_t{T}_h{H}_i{I}_e{E}_k{k}", 420 + i, T, H, I, E, k))
+    return out
+
+
+@pytest.mark.parametrize("case", _layer_sweep_cases(), ids=lambda c: c[0])
+def test_layer_entry_random_shapes(case):
+    name, wid, T, H, I, E, k = case
+    wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
+    x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+    ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, 0))
+    _say("layer entry sweep", name)
+    got = _layer_entry(wl, x, L, stage_weights(wl, 0, ref["perm"]["active"]))
+    check_routing_and_perm(got, ref)
+    assert_close(got["y"], ref["y"], "y")
+    assert_close(got["out"], ref["out"], "out")
+
+
 @pytest.mark.parametrize("name,unit", [("decode_t2", 0), ("decode_t2", 17), ("decode_large", 5),
                                        ("tiny", 0)])
 def test_layer_entry_workloads(name, unit):
