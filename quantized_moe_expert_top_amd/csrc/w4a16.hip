@@ -242,42 +242,49 @@ struct GemvStore {
   }
 };
 
-// One block's GEMV work for expert e, output tile `tile`.
+// One block's GEMV work for expert e, output tile `tile`, in two steps:
+// issue() requests the block's first batch of codes (it needs e and the tile
+// only), run() stages what is left and computes.
 //   A:    KIND 0: x [T][K] (all T rows are staged, x_staged tells whether the
 //         caller already did it); KIND 1: h [R][K] (rows p0.. are staged here).
 //   sorted: flat slot of each of the expert's M rows (global or LDS); row m
 //   is grouped row p0 + m.
-// Returns M (rows of the expert) so callers can run epilogues.
 template <int KIND, int LK, int NB, bool PIPE, int NTHR = kThreads>
-__device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
-                                           const uint8_t* __restrict__ W,
-                                           const uint16_t* __restrict__ S, int e, int tile,
-                                           int p0, int M, const int* sorted, int K, int N,
-                                           int topk, int T, bool x_staged, uint32_t* xs,
-                                           float* bsum, int* tok, const GemvStore& st) {
-  constexpr int MAXM = kGemvMaxM;
-  constexpr int G = GemvGeom<KIND, LK, NTHR>::G;
-  constexpr int UB = GemvGeom<KIND, LK, NTHR>::UB;
-  const int C = K / 32;     // 16-byte code chunks per row
-  const int nch = C / LK;   // chunks per lane (uniform)
-  const int units = N / 2;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
-  const int g = lane / LK, lk = lane % LK;
-  const int u = tile * UB + wv * G + g;
-  const bool valid = u < units;
-  const int uc = valid ? u : units - 1;
-  const int r0 = (KIND == 0) ? uc : 2 * uc;
-  const int r1 = (KIND == 0) ? N / 2 + uc : 2 * uc + 1;
-  const size_t rowb = static_cast<size_t>(K / 2), rows = static_cast<size_t>(K / kGroup);
-  const uint8_t* W0 = W + (static_cast<size_t>(e) * N + r0) * rowb + lk * 16;
-  const uint8_t* W1 = W + (static_cast<size_t>(e) * N + r1) * rowb + lk * 16;
-  const uint16_t* S0 = S + (static_cast<size_t>(e) * N + r0) * rows;
-  const uint16_t* S1 = S + (static_cast<size_t>(e) * N + r1) * rows;
-
+struct GemvBlock {
+  static constexpr int MAXM = kGemvMaxM;
+  static constexpr int G = GemvGeom<KIND, LK, NTHR>::G;
+  static constexpr int UB = GemvGeom<KIND, LK, NTHR>::UB;
+  int C, nch, lk, u;
+  bool valid;
+  const uint8_t* W0;
+  const uint8_t* W1;
+  const uint16_t* S0;
+  const uint16_t* S1;
   uint4 qa0[NB], qa1[NB], qb0[NB], qb1[NB];
   uint32_t sa[NB], sb[NB];  // raw fp16 scales: low half row 0, high half row 1
-  auto load_batch = [&](int i0, uint4 (&q0)[NB], uint4 (&q1)[NB], uint32_t (&sc)[NB]) {
+
+  __device__ __forceinline__ GemvBlock(const uint8_t* __restrict__ W,
+                                       const uint16_t* __restrict__ S, int e, int tile, int K,
+                                       int N) {
+    C = K / 32;     // 16-byte code chunks per row
+    nch = C / LK;   // chunks per lane (uniform)
+    const int units = N / 2;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+    const int g = lane / LK;
+    lk = lane % LK;
+    u = tile * UB + wv * G + g;
+    valid = u < units;
+    const int uc = valid ? u : units - 1;
+    const int r0 = (KIND == 0) ? uc : 2 * uc;
+    const int r1 = (KIND == 0) ? N / 2 + uc : 2 * uc + 1;
+    const size_t rowb = static_cast<size_t>(K / 2), rows = static_cast<size_t>(K / kGroup);
+    W0 = W + (static_cast<size_t>(e) * N + r0) * rowb + lk * 16;
+    W1 = W + (static_cast<size_t>(e) * N + r1) * rowb + lk * 16;
+    S0 = S + (static_cast<size_t>(e) * N + r0) * rows;
+    S1 = S + (static_cast<size_t>(e) * N + r1) * rows;
+  }
+  __device__ __forceinline__ void load_batch(int i0, uint4 (&q0)[NB], uint4 (&q1)[NB],
+                                             uint32_t (&sc)[NB]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int i = PIPE ? min(i0 + b, nch - 1) : b;
@@ -290,100 +297,117 @@ __device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
       const int c = lk + i * LK;
       sc[b] = static_cast<uint32_t>(S0[c >> 2]) | (static_cast<uint32_t>(S1[c >> 2]) << 16);
     }
-  };
-  load_batch(0, qa0, qa1, sa);
-  if (KIND == 0 && !x_staged) gemv_stage(A, T, K, xs, bsum);
+  }
+  __device__ __forceinline__ void issue() { load_batch(0, qa0, qa1, sa); }
 
-  const NibbleConsts nk = nibble_consts();
-  auto finish = [&](float acc0, float acc1, int m) {
-#pragma unroll
-    for (int sh = LK / 2; sh >= 1; sh >>= 1) {
-      acc0 += wave_shfl_xor(acc0, sh);
-      acc1 += wave_shfl_xor(acc1, sh);
-    }
-    if (lk == 0 && valid) st.put<KIND>(static_cast<size_t>(p0 + m), u, acc0, acc1);
-  };
+  __device__ __forceinline__ void run(const uint16_t* __restrict__ A, int p0, int M,
+                                      const int* sorted, int K, int topk, int T, bool x_staged,
+                                      uint32_t* xs, float* bsum, int* tok, const GemvStore& st) {
+    const int tid = threadIdx.x;
+    if (KIND == 0 && !x_staged) gemv_stage(A, T, K, xs, bsum);
 
-  // rows are taken in chunks of MAXM (normally one chunk: M <= T <= 4)
-  for (int m0 = 0; m0 < M; m0 += MAXM) {
-    const int Mc = min(MAXM, M - m0);
-    if (KIND == 0) {
-      if (tid < Mc) tok[tid] = sorted[m0 + tid] / topk;
-    } else {
-      gemv_stage(A + static_cast<size_t>(p0 + m0) * K, Mc, K, xs, bsum);
-    }
-    __syncthreads();
-    if (!PIPE) {
-      // all of this lane's codes are in registers: one pass over them for
-      // all rows of the chunk
-      for_row_pairs(Mc, [&](int mb, auto mm) __attribute__((always_inline)) {
-        constexpr int MM = decltype(mm)::value;
-        int xr[MM];
+    const NibbleConsts nk = nibble_consts();
+    auto finish = [&](float acc0, float acc1, int m) {
 #pragma unroll
-        for (int m = 0; m < MM; ++m) xr[m] = (KIND == 0) ? tok[mb + m] : mb + m;
-        uint32_t s0a[NB], s1a[NB];
+      for (int sh = LK / 2; sh >= 1; sh >>= 1) {
+        acc0 += wave_shfl_xor(acc0, sh);
+        acc1 += wave_shfl_xor(acc1, sh);
+      }
+      if (lk == 0 && valid) st.put<KIND>(static_cast<size_t>(p0 + m), u, acc0, acc1);
+    };
+    // rows are taken in chunks of MAXM (normally one chunk: M <= T <= 4)
+    for (int m0 = 0; m0 < M; m0 += MAXM) {
+      const int Mc = min(MAXM, M - m0);
+      if (KIND == 0) {
+        if (tid < Mc) tok[tid] = sorted[m0 + tid] / topk;
+      } else {
+        gemv_stage(A + static_cast<size_t>(p0 + m0) * K, Mc, K, xs, bsum);
+      }
+      __syncthreads();
+      if (!PIPE) {
+        // all of this lane's codes are in registers: one pass over them for
+        // all rows of the chunk
+        for_row_pairs(Mc, [&](int mb, auto mm) __attribute__((always_inline)) {
+          constexpr int MM = decltype(mm)::value;
+          int xr[MM];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          s0a[b] = sa[b];
-          s1a[b] = sa[b] >> 16;
-        }
-        float acc0[MM], acc1[MM];
-        gemv_rows<MM, LK, NB>(qa0, qa1, s0a, s1a, xs, bsum, K / 2, C, xr, lk, nk, acc0, acc1);
-        if (lk == 0 && valid) {
-#pragma unroll
-          for (int m = 0; m < MM; ++m)
-            st.put<KIND>(static_cast<size_t>(p0 + m0 + mb + m), u, acc0[m], acc1[m]);
-        }
-      });
-    } else {
-      // codes stream through two register batches; rows two at a time, the
-      // codes widened once for both
-      for (int mp = 0; mp < Mc; mp += 2) {
-        const bool two = mp + 1 < Mc;
-        const int xr0 = (KIND == 0) ? tok[mp] : mp;
-        const int xr1 = two ? ((KIND == 0) ? tok[mp + 1] : mp + 1) : xr0;
-        const uint32_t* xrow1[1] = {xs + xr0 * (K / 2)};
-        const uint32_t* xrow2[2] = {xs + xr0 * (K / 2), xs + xr1 * (K / 2)};
-        float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-        auto compute_batch = [&](int i0, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
-                                 const uint32_t (&sc)[NB]) {
+          for (int m = 0; m < MM; ++m) xr[m] = (KIND == 0) ? tok[mb + m] : mb + m;
+          uint32_t s0a[NB], s1a[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
-            if (i0 + b < nch) {
-              const int c = lk + (i0 + b) * LK;
-              const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu));
-              const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16));
-              const float cs0 = bsum[xr0 * C + c];
-              if (two) {
-                float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
-                dot_chunk_rows<2>(q0[b], q1[b], xrow2, c, C, nk, d0, d1);
-                const float cs1 = bsum[xr1 * C + c];
-                acc[0][0] += s0 * (d0[0] - cs0);
-                acc[0][1] += s1 * (d1[0] - cs0);
-                acc[1][0] += s0 * (d0[1] - cs1);
-                acc[1][1] += s1 * (d1[1] - cs1);
-              } else {
-                float d0[1] = {0.0f}, d1[1] = {0.0f};
-                dot_chunk_rows<1>(q0[b], q1[b], xrow1, c, C, nk, d0, d1);
-                acc[0][0] += s0 * (d0[0] - cs0);
-                acc[0][1] += s1 * (d1[0] - cs0);
+            s0a[b] = sa[b];
+            s1a[b] = sa[b] >> 16;
+          }
+          float acc0[MM], acc1[MM];
+          gemv_rows<MM, LK, NB>(qa0, qa1, s0a, s1a, xs, bsum, K / 2, C, xr, lk, nk, acc0, acc1);
+          if (lk == 0 && valid) {
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+              st.put<KIND>(static_cast<size_t>(p0 + m0 + mb + m), u, acc0[m], acc1[m]);
+          }
+        });
+      } else {
+        // codes stream through two register batches; rows two at a time, the
+        // codes widened once for both
+        for (int mp = 0; mp < Mc; mp += 2) {
+          const bool two = mp + 1 < Mc;
+          const int xr0 = (KIND == 0) ? tok[mp] : mp;
+          const int xr1 = two ? ((KIND == 0) ? tok[mp + 1] : mp + 1) : xr0;
+          const uint32_t* xrow1[1] = {xs + xr0 * (K / 2)};
+          const uint32_t* xrow2[2] = {xs + xr0 * (K / 2), xs + xr1 * (K / 2)};
+          float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+          auto compute_batch = [&](int i0, const uint4 (&q0)[NB], const uint4 (&q1)[NB],
+                                   const uint32_t (&sc)[NB]) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              if (i0 + b < nch) {
+                const int c = lk + (i0 + b) * LK;
+                const float s0 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] & 0xFFFFu));
+                const float s1 = fp16_bits_to_f32(static_cast<uint16_t>(sc[b] >> 16));
+                const float cs0 = bsum[xr0 * C + c];
+                if (two) {
+                  float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
+                  dot_chunk_rows<2>(q0[b], q1[b], xrow2, c, C, nk, d0, d1);
+                  const float cs1 = bsum[xr1 * C + c];
+                  acc[0][0] += s0 * (d0[0] - cs0);
+                  acc[0][1] += s1 * (d1[0] - cs0);
+                  acc[1][0] += s0 * (d0[1] - cs1);
+                  acc[1][1] += s1 * (d1[1] - cs1);
+                } else {
+                  float d0[1] = {0.0f}, d1[1] = {0.0f};
+                  dot_chunk_rows<1>(q0[b], q1[b], xrow1, c, C, nk, d0, d1);
+                  acc[0][0] += s0 * (d0[0] - cs0);
+                  acc[0][1] += s1 * (d1[0] - cs0);
+                }
               }
             }
+          };
+          if (m0 != 0 || mp != 0) load_batch(0, qa0, qa1, sa);   // first pass reuses the prefetch
+          for (int i0 = 0; i0 < nch; i0 += 2 * NB) {
+            if (i0 + NB < nch) load_batch(i0 + NB, qb0, qb1, sb);
+            compute_batch(i0, qa0, qa1, sa);
+            if (i0 + 2 * NB < nch) load_batch(i0 + 2 * NB, qa0, qa1, sa);
+            if (i0 + NB < nch) compute_batch(i0 + NB, qb0, qb1, sb);
           }
-        };
-        if (m0 != 0 || mp != 0) load_batch(0, qa0, qa1, sa);   // first pass reuses the prefetch
-        for (int i0 = 0; i0 < nch; i0 += 2 * NB) {
-          if (i0 + NB < nch) load_batch(i0 + NB, qb0, qb1, sb);
-          compute_batch(i0, qa0, qa1, sa);
-          if (i0 + 2 * NB < nch) load_batch(i0 + 2 * NB, qa0, qa1, sa);
-          if (i0 + NB < nch) compute_batch(i0 + NB, qb0, qb1, sb);
+          finish(acc[0][0], acc[0][1], m0 + mp);
+          if (two) finish(acc[1][0], acc[1][1], m0 + mp + 1);
         }
-        finish(acc[0][0], acc[0][1], m0 + mp);
-        if (two) finish(acc[1][0], acc[1][1], m0 + mp + 1);
       }
+      __syncthreads();  // tok / LDS rows are rewritten by the next row chunk
     }
-    __syncthreads();  // tok / LDS rows are rewritten by the next row chunk
   }
+};
+
+template <int KIND, int LK, int NB, bool PIPE, int NTHR = kThreads>
+__device__ __forceinline__ void gemv_block(const uint16_t* __restrict__ A,
+                                           const uint8_t* __restrict__ W,
+                                           const uint16_t* __restrict__ S, int e, int tile,
+                                           int p0, int M, const int* sorted, int K, int N,
+                                           int topk, int T, bool x_staged, uint32_t* xs,
+                                           float* bsum, int* tok, const GemvStore& st) {
+  GemvBlock<KIND, LK, NB, PIPE, NTHR> b(W, S, e, tile, K, N);
+  b.issue();
+  b.run(A, p0, M, sorted, K, topk, T, x_staged, xs, bsum, tok, st);
 }
 
 // Dynamic LDS of a GEMV block: staged rows (pair-permuted) + bias sums.
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
   const int na = *n_active;
   const int e = active[a];  // in bounds: the grid has min(E, R) slots
   if (a >= na) return;      // uniform per block, before any barrier
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int rows_staged = (KIND == 0) ? T : kGemvMaxM;
   uint32_t* xs = lds;
   float* bsum = reinterpret_cast<float*>(lds + rows_staged * (K / 2));
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(NTHR) void decode_gateup_slot_kernel(
     int* __restrict__ offsets_out, int* __restrict__ sorted_out, int* __restrict__ pos_out,
     int* __restrict__ active_out, int* __restrict__ n_active_out, uint16_t* __restrict__ h,
     int* __restrict__ rec) {
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* xs = lds;                                            // [T][H/2]
   float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][H/32]
   int* s_off = reinterpret_cast<int*>(bsum + T * (H / 32));      // [E + 1] (bookkeeping)
@@ -613,7 +637,7 @@ __global__ __launch_bounds__(NTHR, 4 * kThreads / NTHR) void decode_gateup_kerne
     int* __restrict__ n_active_out, uint16_t* __restrict__ h, int* __restrict__ rec) {
   constexpr int G = kWave / LK;                  // lane groups per wave
   constexpr int NGB = (NTHR / kWave) * G;        // lane groups per block
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int C = H / 32;                                          // 16-byte chunks per row
   uint32_t* xs = lds;                                            // [T][H/2]
   float* bsum = reinterpret_cast<float*>(lds + T * (H / 2));     // [T][C]
@@ -749,7 +773,7 @@ __global__ __launch_bounds__(NTHR, NTHR > kThreads ? 4 * kThreads / NTHR : 1) vo
     const float* __restrict__ topk_w, float* __restrict__ y, float* __restrict__ out) {
   constexpr int G = kWave / LK;       // lane groups per wave
   constexpr int NG = (NTHR / kWave) * G;   // lane groups per block
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int R = T * k;
   const int C = I / 32;
   const int nr = 2 * upb;                                        // rows of H in this tile
@@ -1134,7 +1158,7 @@ __global__ __launch_bounds__(kThreads, MT == 1 ? 2 : 1) void w4a16_mfma_kernel(
   __shared__ int row_src[BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[5];
-  extern __shared__ uint16_t s_lds[];   // [256][G]: fp16 scales of the tile's weight rows
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_lds[];  // [256][G]: fp16 scales of the tile's weight rows
 
   TileInfo ti;
   if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;

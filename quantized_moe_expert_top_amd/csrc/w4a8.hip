@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a8_mfma_kernel(
   __shared__ float row_scale[BM];
   __shared__ int sm_pref[kThreads / kWave];
   __shared__ int sm_out[5];
-  extern __shared__ uint16_t s_lds[];   // [256][G]: fp16 scales of the tile's weight rows
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_lds[];  // [256][G]: fp16 scales of the tile's weight rows
 
   TileInfo ti;
   if (!find_tile<BM>(offsets, E, NT, sm_pref, sm_out, ti)) return;
