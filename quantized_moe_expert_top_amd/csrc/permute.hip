@@ -185,7 +185,7 @@ __global__ __launch_bounds__(NTHR) void permute_small_kernel(
     int* __restrict__ sorted_slot, int* __restrict__ slot_pos, int* __restrict__ active,
     int* __restrict__ n_active) {
   constexpr int NW = NTHR / kWave;
-  extern __shared__ int sm[];
+  extern __shared__ __attribute__((aligned(16))) int sm[];
   int* counts = sm;            // [E]
   int* run = counts + E;       // [E]
   int* wc = run + E;           // [NW][E]: per-wave counts, then prefixes over waves
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(NTHR) void permute_small_kernel(
 __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int* __restrict__ ids,
                                                                 int R, int E,
                                                                 int* __restrict__ hist) {
-  extern __shared__ int counts[];
+  extern __shared__ __attribute__((aligned(16))) int counts[];
   for (int i = threadIdx.x; i < E; i += kThreads) counts[i] = 0;
   __syncthreads();
   const int base = blockIdx.x * kChunk;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int* __res
 __global__ __launch_bounds__(kThreads) void permute_scan_kernel(
     const int* __restrict__ hist, int* __restrict__ bases, int NB, int R, int E,
     int* __restrict__ offsets, int* __restrict__ active, int* __restrict__ n_active) {
-  extern __shared__ int sm[];
+  extern __shared__ __attribute__((aligned(16))) int sm[];
   int* counts = sm;       // [E]
   int* run = sm + E;      // [E]
   __shared__ int wave_tot[kWaves];
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
     const int* __restrict__ ids, const int* __restrict__ bases,
     const int* __restrict__ offsets, int R, int E, int* __restrict__ sorted_slot,
     int* __restrict__ slot_pos) {
-  extern __shared__ int sm[];
+  extern __shared__ __attribute__((aligned(16))) int sm[];
   int* run = sm;          // [E]
   int* wc = sm + E;       // [kWaves * E]
   for (int e = threadIdx.x; e < E; e += kThreads)

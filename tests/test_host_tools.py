@@ -109,6 +109,26 @@ def test_built_objects_came_with_no_spills():
     assert build.spilling(res) == {}
 
 
+def test_dynamic_lds_arrays_are_16_byte_aligned():
+    """A kernel's dynamic LDS starts where its static LDS ends, aligned only to
+    the declared alignment of the extern array. The GEMV and GEMM kernels read
+    their staged rows with 16-byte LDS loads, and a 4-byte static variable once
+    left them on a 4-byte boundary (the decode gate/up kernel ran 20% slower),
+    so every dynamic LDS array is declared 16-byte aligned."""
+    import re
+    csrc = os.path.join(ROOT, "quantized_moe_expert_top_amd", "csrc")
+    decls = []
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name)) as f:
+                for i, line in enumerate(f, 1):
+                    if re.search(r"\bextern\s+__shared__\b", line):
+                        decls.append((name, i, line.strip()))
+    assert len(decls) >= 7
+    bad = [d for d in decls if "aligned(16)" not in d[2]]
+    assert bad == []
+
+
 def test_trace_summary_counts_only_the_marked_range(tmp_path):
     """trace_summary keeps the dispatches that start inside the named roctx
     range (the timed graph replays) and drops the rest (eager pass, warmup)."""
