@@ -151,11 +151,20 @@ template <int S>  // key slots per lane: E <= 64 * S
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int* ids,
                                           float* w) {
   const int lane = threadIdx.x & (kWave - 1);
+  // every slot's logit is requested before any is used (slots past E read
+  // the last logit and get key 0), so the row costs one memory round trip:
+  // a guarded load per slot had compiled to S loads each waited on in turn
+  float v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = lane + kWave * s;
+    v[s] = row[e < E ? e : E - 1];
+  }
   uint64_t key[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e = lane + kWave * s;
-    key[s] = (e < E) ? route_key(row[e], e) : 0ull;  // valid keys are > 0
+    key[s] = (e < E) ? route_key(v[s], e) : 0ull;  // valid keys are > 0
   }
   int my_e = 0;
   float my_l = 0.0f;
