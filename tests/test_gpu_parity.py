@@ -516,6 +516,42 @@ def test_layer_entry_matches_oracle_and_calls(case):
     np.testing.assert_array_equal(got["out_bits"], calls["out_bits"])
 
 
+PREFILL_LAYER_CASES = [
+    # name, wid, T, H, I, E, k, router bias
+    ("lp_t512", 331, 512, 2048, 768, 128, 8, "normal"),   # the prompt shape: 4096 routed slots
+    ("lp_t40_e1024", 332, 40, 256, 256, 1024, 8, "normal"),   # the largest E
+    ("lp_t64_k32", 333, 64, 256, 256, 64, 32, "normal"),   # 2048 slots at k 32
+    ("lp_t33_e1", 334, 33, 256, 256, 1, 1, "none"),        # every token on one expert
+    ("lp_t520", 335, 520, 256, 256, 64, 8, "normal"),      # 4160 slots, ragged m-tiles
+]
+# (I >= 256: below it the bf16 rounding of h alone moves single y elements
+# past 2% of the row rms, as at _sweep_cases)
+
+
+@pytest.mark.parametrize("case", PREFILL_LAYER_CASES, ids=[c[0] for c in PREFILL_LAYER_CASES])
+def test_layer_entry_prefill_matches_calls(case):
+    """Prefill shapes (T > 4) through the whole-layer entry: routing,
+    permutation, y and out are bit for bit those of the separate calls (route,
+    permute, grouped FFN, combine); the smaller cases also against the
+    oracle."""
+    name, wid, T, H, I, E, k, bias = case
+    wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", bias, 1)
+    x, L = synth.x_bf16(wl, 0), synth.router_logits(wl, 0)
+    wts = stage_weights(wl, 0)
+    _say("prefill layer entry", name, (T, H, I, E, k))
+    got = _layer_entry(wl, x, L, wts)
+    calls = run_layer(wl, x, L, wts)
+    for key in ("ids", "expert_offsets", "sorted_slot", "slot_pos", "active", "y_bits",
+                "out_bits"):
+        np.testing.assert_array_equal(got[key], calls[key], err_msg=key)
+    assert got["n_active"] == calls["n_active"]
+    if T * H <= 64 * 1024:
+        ref = oracle.moe_layer_w4a16(x, L, wl.k, expert_getter_w4(wl, 0))
+        check_routing_and_perm(got, ref)
+        assert_close(got["y"], ref["y"], "y")
+        assert_close(got["out"], ref["out"], "out")
+
+
 def _layer_sweep_cases(n=10, seed=2027):
     """Seeded random decode shapes for the whole-layer entry (T <= 4, the fused
     kernels): H up to 3072 and I from 256 in steps of 128, E from 1 to 300,
@@ -657,6 +693,7 @@ INVARIANCE_CASES = [
     (4, 2, "layer"),
     (40, 20, "calls"),
     (512, 128, "calls"),   # the prompt shape on the MFMA GEMMs, against four batches of 128
+    (512, 128, "layer"),   # the same through the layer entry
 ]
 
 
