@@ -472,6 +472,13 @@ def test_empty_batch_all_entry_points():
         moe.moe_forward(b, x, L, (dummy, dummy, dummy, dummy))
         torch.cuda.synchronize()
         assert np.all(to_np(b.offsets) == 0) and int(to_np(b.n_active)[0]) == 0
+    # the whole-layer entry with no token: offsets all zero, no active expert
+    b = moe.LayerBuffers.alloc(0, 256, 128, 8, 2, "w4a16")
+    b.offsets.fill_(-1)
+    b.n_active.fill_(-1)
+    moe.moe_layer(b, x, L, (dummy, dummy, dummy, dummy))
+    torch.cuda.synchronize()
+    assert np.all(to_np(b.offsets) == 0) and int(to_np(b.n_active)[0]) == 0
 
 
 # ------------------------------------------------------------ whole layer --
