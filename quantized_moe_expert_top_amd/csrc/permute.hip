@@ -74,6 +74,39 @@ __device__ __forceinline__ int block_excl_scan_n(int v, int* wave_tot, int& tota
 template <int NTHR>
 __device__ void offsets_and_active(const int* counts, int* run, int E, int R, int* wave_tot,
                                    int* offsets, int* active, int* n_active) {
+  if (E <= 4 * kWave && R < (1 << 16)) {   // uniform
+    // wave 0 alone, four experts a lane, with no block barrier: one scan of
+    // count (low 16 bits, sum <= R) and active flag (high bits) packed together
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      int c[4], v = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        c[i] = e < E ? counts[e] : 0;
+        v += c[i] + (c[i] > 0 ? (1 << 16) : 0);
+      }
+      const int incl = wave_incl_scan(v);
+      const int excl = incl - v;
+      int oc = excl & 0xFFFF, of = excl >> 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        if (e < E) {
+          run[e] = oc;
+          offsets[e] = oc;
+          if (c[i]) active[of] = e;
+        }
+        oc += c[i];
+        of += c[i] > 0;
+      }
+      if (lane == kWave - 1) {
+        offsets[E] = R;
+        *n_active = incl >> 16;
+      }
+    }
+    return;
+  }
   const int ept = (E + NTHR - 1) / NTHR;  // <= 4
   const int e0 = threadIdx.x * ept;
   int c[4], f[4], sc = 0, sf = 0;
