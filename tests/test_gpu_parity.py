@@ -98,7 +98,10 @@ def _random_ids(T, E, k, seed, skew=0.0):
 @pytest.mark.parametrize("T,E,k,skew", [(16, 8, 2, 0), (2, 128, 8, 0), (129, 128, 8, 0),
                                         (4096, 128, 8, 0), (4096, 128, 8, 2.0), (64, 1024, 32, 0),
                                         (1, 1, 1, 0), (1000, 3, 3, 0), (300, 256, 8, 1.1),
-                                        (1024, 128, 8, 0.5), (2731, 64, 3, 0), (20, 512, 32, 0)])
+                                        (1024, 128, 8, 0.5), (2731, 64, 3, 0), (20, 512, 32, 0),
+                                        # the one-wave offsets scan up to E 256 and R < 65536,
+                                        # the block scan past either bound
+                                        (8191, 128, 8, 0), (8192, 128, 8, 0), (100, 257, 4, 0)])
 def test_permute_matches_oracle(T, E, k, skew):
     ids = _random_ids(T, E, k, T + E, skew)
     _say("permute", T, E, k, skew)
