@@ -395,6 +395,12 @@ __global__ __launch_bounds__(G::kThreads, G::kBlocksPerCU) void w8a8_mfma_kernel
     __builtin_amdgcn_sched_group_barrier(0x100, (BK / 32) * (MI + NJ), 0);
     __builtin_amdgcn_sched_group_barrier(0x008, (BK / 32) * MI * NJ, 0);
   };
+  // An expert's last m-tile often holds only a few rows (at T 4096 about a
+  // fifth of the tiles hold 32 rows or fewer): a wave whose row band lies past
+  // the expert's rows takes no LDS reads and no MFMAs (its accumulators stay
+  // zero and their stores are dropped); every other wave computes as usual.
+  const bool band_live =
+      __builtin_amdgcn_readfirstlane(wm) * RW < ti.p_end - ti.p_begin;   // uniform per wave
 
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(G::kThreads, G::kBlocksPerCU) void w8a8_mfma_kernel
     // stage st is complete once at most the later in-flight stages remain
     wait_stage<G::kLoadsPerStage, STAGES - 2>(min(STAGES - 2, steps - 1 - st));
     if (st + STAGES - 1 < steps) issue(st + STAGES - 1);
-    compute(w8_lds + (st % STAGES) * G::kStageBytes);
+    if (band_live) compute(w8_lds + (st % STAGES) * G::kStageBytes);
   }
 
   // epilogue. C layout of a 32 x 32 subtile: lane holds column l32, rows
