@@ -157,3 +157,27 @@ def test_trace_summary_counts_only_the_marked_range(tmp_path):
     assert "| `b_kernel` | 1 | 0.03 | 0.0 | 50.0% |" in trace_summary.markdown(s)
     with pytest.raises(SystemExit):
         trace_summary.summarize(str(db), "no such range", 1)
+
+
+def test_bench_algorithmic_bytes_and_roofline_math():
+    """The roofline unit's bytes are the routed experts' packed weights and
+    scales plus the layer's x, logits and out; frac is those bytes over the
+    unit's average time against the 8 TB/s peak, and the MFMA fraction is the
+    layer's 6*T*k*H*I operations against the dense peak of the path's type."""
+    import bench
+    import synth
+    w4 = synth.workload("decode_t2")
+    assert bench.expert_bytes(w4) == 2_433_024            # H 2048, I 768, int4 g128 + fp16 scales
+    assert bench.expert_bytes(synth.workload("decode_large")) == 22_708_224
+    w8 = synth.workload("w8a8_t4096")
+    assert bench.expert_bytes(w8) == 4_732_928            # int8 + float32 per-channel scales
+    assert bench.io_bytes(w4) == 2 * 2048 * 2 + 2 * 128 * 4 + 2 * 2048 * 4
+    fake = w8.with_(name="w8a8_fake_for_test")            # no stored traffic entry
+    m = {"wl": fake, "avg_bytes": 658_243_584, "avg_ms": 0.36, "kernel": "k", "cold_ms": None,
+         "flops_per_call": 6 * fake.T * fake.k * fake.H * fake.I}
+    r = bench.roofline(m)
+    achieved = 658_243_584 / 0.36e-3 / 1e9
+    assert r["achieved"] == round(achieved, 1)
+    assert r["frac"] == round(achieved / 8000.0, 4)
+    assert r["traffic"] is None and r["avg_launch_us"] == 360.0
+    assert r["mfma_frac"] == round(m["flops_per_call"] / 0.36e-3 / 1e12 / 5000.0, 4)
