@@ -430,7 +430,7 @@ def test_w4a8_deterministic():
     np.testing.assert_array_equal(a["out_bits"], b["out_bits"])
 
 
-def _sweep_cases(n=12, seed=2026):
+def _sweep_cases(n=12, seed=2026, tag="sweep", wid0=400):
     """Seeded random layer shapes over the three formats, small enough for the
     float64 oracle: T past the decode GEMV (MFMA paths), W4 dims multiples of
     128, W8A8 dims multiples of 16, E from 1 to 64, k up to min(E, 8), skewed
@@ -448,11 +448,12 @@ def _sweep_cases(n=12, seed=2026):
         I = step * int(rng.integers(2 if fmt == "w4a16" else 1, 768 // step + 1))
         E = int(rng.integers(1, 65))
         k = int(rng.integers(1, min(E, 8) + 1))
-        out.append((f"sweep{i}_{fmt}_t{T}_h{H}_i{I}_e{E}_k{k}", 400 + i, T, H, I, E, k, fmt))
+        out.append((f"{tag}{i}_{fmt}_t{T}_h{H}_i{I}_e{E}_k{k}", wid0 + i, T, H, I, E, k, fmt))
     return out
 
 
-@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: c[0])
+@pytest.mark.parametrize("case", _sweep_cases() + _sweep_cases(30, 3031, "wsweep", 900),
+                         ids=lambda c: c[0])
 def test_random_shapes_sweep(case):
     name, wid, T, H, I, E, k, fmt = case
     bias = "none" if fmt == "w8a8" else "normal"
@@ -562,7 +563,7 @@ def test_layer_entry_prefill_matches_calls(case):
         assert_close(got["out"], ref["out"], "out")
 
 
-def _layer_sweep_cases(n=10, seed=2027):
+def _layer_sweep_cases(n=10, seed=2027, tag="lsweep", wid0=420):
     """Seeded random decode shapes for the whole-layer entry (T <= 4, the fused
     kernels): H up to 3072 and I from 256 in steps of 128, E from 1 to 300,
     k up to min(E, 16); slot-per-block and persistent gate/up and every lane
@@ -575,11 +576,12 @@ def _layer_sweep_cases(n=10, seed=2027):
         I = 128 * int(rng.integers(2, 9))
         E = int(rng.integers(1, 301))
         k = int(rng.integers(1, min(E, 16) + 1))
-        out.append((f"lsweep{i}_t{T}_h{H}_i{I}_e{E}_k{k}", 420 + i, T, H, I, E, k))
+        out.append((f"{tag}{i}_t{T}_h{H}_i{I}_e{E}_k{k}", wid0 + i, T, H, I, E, k))
     return out
 
 
-@pytest.mark.parametrize("case", _layer_sweep_cases(), ids=lambda c: c[0])
+@pytest.mark.parametrize("case", _layer_sweep_cases() + _layer_sweep_cases(20, 3033, "wlsweep", 940),
+                         ids=lambda c: c[0])
 def test_layer_entry_random_shapes(case):
     name, wid, T, H, I, E, k = case
     wl = synth.Workload(name, wid, T, H, I, E, k, "w4a16", "normal", 1)
