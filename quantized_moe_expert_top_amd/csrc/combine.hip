@@ -9,6 +9,27 @@
 namespace moe {
 namespace {
 
+// Each thread owns 8 consecutive floats of one token's row. The picks are
+// taken in full batches of kJB: a batch's slot positions and weights are
+// loaded together, then all of its y reads are issued before the first is
+// used, so the batch costs one round trip to memory for the positions and one
+// for the rows (loading and adding one pick at a time waits k times). Picks
+// left over past the last full batch go one at a time. The adds run in
+// increasing j either way.
+constexpr int kJB = 8;
+
+__device__ __forceinline__ void add_pick(float (&acc)[8], float wj, const float4& a,
+                                         const float4& b) {
+  acc[0] += wj * a.x;
+  acc[1] += wj * a.y;
+  acc[2] += wj * a.z;
+  acc[3] += wj * a.w;
+  acc[4] += wj * b.x;
+  acc[5] += wj * b.y;
+  acc[6] += wj * b.z;
+  acc[7] += wj * b.w;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int* __restrict__ slot_pos,
                                                       const float* __restrict__ w, int T, int H,
@@ -18,20 +39,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (idx >= static_cast<long long>(T) * chunks) return;
   const int t = static_cast<int>(idx / chunks);
   const int c = static_cast<int>(idx % chunks);
+  const int* sp = slot_pos + static_cast<size_t>(t) * k;
+  const float* wt = w + static_cast<size_t>(t) * k;
+  const float* yc = y + c * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[static_cast<size_t>(t) * k + j];
-    const int p = slot_pos[static_cast<size_t>(t) * k + j];
-    const float4* src = reinterpret_cast<const float4*>(y + static_cast<size_t>(p) * H + c * 8);
-    const float4 a = src[0], b = src[1];
-    acc[0] += wj * a.x;
-    acc[1] += wj * a.y;
-    acc[2] += wj * a.z;
-    acc[3] += wj * a.w;
-    acc[4] += wj * b.x;
-    acc[5] += wj * b.y;
-    acc[6] += wj * b.z;
-    acc[7] += wj * b.w;
+  int j0 = 0;
+  for (; j0 + kJB <= k; j0 += kJB) {
+    int p[kJB];
+    float wj[kJB];
+#pragma unroll
+    for (int u = 0; u < kJB; ++u) {
+      p[u] = sp[j0 + u];
+      wj[u] = wt[j0 + u];
+    }
+    float4 a[kJB], b[kJB];
+#pragma unroll
+    for (int u = 0; u < kJB; ++u) {
+      const float4* src = reinterpret_cast<const float4*>(yc + static_cast<size_t>(p[u]) * H);
+      a[u] = src[0];
+      b[u] = src[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all of the batch's reads go out first
+#pragma unroll
+    for (int u = 0; u < kJB; ++u) add_pick(acc, wj[u], a[u], b[u]);
+  }
+  for (int j = j0; j < k; ++j) {
+    const float4* src = reinterpret_cast<const float4*>(yc + static_cast<size_t>(sp[j]) * H);
+    add_pick(acc, wt[j], src[0], src[1]);
   }
   float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * H + c * 8);
   o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

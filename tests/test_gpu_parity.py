@@ -118,10 +118,13 @@ def test_permute_empty_batch():
 
 
 # ----------------------------------------------------------------- combine --
-def test_combine_matches_oracle():
+@pytest.mark.parametrize("k", [1, 5, 8, 13, 16, 32])
+def test_combine_matches_oracle(k):
+    # k below, at and past the kernel's batch of eight picks, with a partial
+    # batch after full ones (13) and several full batches (16, 32)
     import quantized_moe_expert_top_amd as moe
-    rng = np.random.default_rng(1)
-    T, H, k = 77, 520, 5
+    rng = np.random.default_rng(1 + k)
+    T, H = 77, 520
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     slot_pos = rng.permutation(T * k).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
