@@ -109,6 +109,123 @@ def test_built_objects_came_with_no_spills():
     assert build.spilling(res) == {}
 
 
+def _w8a8_geometry():
+    """kLoadsPerStage and kStages of the tile the W8A8 GEMM is instantiated
+    with, from its source (the same formulas as W8Geom)."""
+    import re
+    with open(os.path.join(ROOT, "quantized_moe_expert_top_amd", "csrc", "w8a8.hip")) as f:
+        src = f.read()
+    m = re.search(r"using W8Tile = W8Geom<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>;", src)
+    assert m, "W8Tile definition not found"
+    bm, wm, wn, bk, stages, _ = (int(v) for v in m.groups())
+    nthr, cpr = wm * wn * 64, bk // 16
+    return (bm * cpr) // nthr + (256 * cpr) // nthr, stages
+
+
+def _loops_of(asm_lines):
+    """{loop header: [instruction lines]} of one function's assembly, from the
+    loop comments LLVM puts on every block label."""
+    import re
+    label = re.compile(r"^(?:(\.LBB\d+_\d+):|; %bb\.\d+:)\s*(?:;\s*(.*))?$")
+    loops, cur = {}, None
+    for line in asm_lines:
+        m = label.match(line.strip())
+        if m:
+            cur = None
+            note = m.group(2) or ""
+            h = re.search(r"in Loop: Header=(BB\d+_\d+)", note)
+            if h:
+                cur = h.group(1)
+            elif "Loop Header" in note and m.group(1):
+                cur = m.group(1)[1:]
+            continue
+        ins = line.strip()
+        if cur and ins and not ins.startswith((";", ".")):
+            loops.setdefault(cur, []).append(ins)
+    return loops
+
+
+def _w8a8_loop_problems(lines, lps, stages):
+    """What breaks the hand-counted waits in the W8A8 GEMM kernels of one
+    assembly listing: [] when, inside each kernel's stage-issuing loop, every
+    vector-memory instruction is a 16-byte buffer load into LDS, they come
+    lps to a stage between waits, and every vmcnt wait lets at most the later
+    stages (stages - 2 of them) stay in flight."""
+    import re
+    starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\w*w8a8_mfma_kernel\w*:", l)]
+    if len(starts) != 2:
+        return [f"{len(starts)} w8a8_mfma_kernel instantiations, expected 2"]
+    vmem = re.compile(r"^(buffer|global|scratch|flat)_\w+")
+    allowed = {lps * n for n in range(stages - 1)}
+    problems = []
+    for s0 in starts:
+        name = lines[s0]
+        end = next(i for i in range(s0, len(lines)) if lines[i].startswith(".Lfunc_end"))
+        body = lines[s0:end]
+        if any(l.strip().startswith("scratch_") for l in body):
+            problems.append(f"{name} uses scratch")
+        loops = {h: ins for h, ins in _loops_of(body).items()
+                 if any(vmem.match(i) and i.endswith(" lds") for i in ins)}
+        if len(loops) != 1:
+            problems.append(f"{name}: {len(loops)} loops issue LDS stages")
+            continue
+        ins = next(iter(loops.values()))
+        other = [i for i in ins if vmem.match(i) and not re.match(r"buffer_load_dwordx4 .* lds$", i)]
+        if other:
+            problems.append(f"{name}: other vector-memory instructions in the loop: {other}")
+        waits = [int(v) for i in ins for v in re.findall(r"vmcnt\((\d+)\)", i)]
+        if not waits or not set(waits) <= allowed:
+            problems.append(f"{name}: vmcnt waits {sorted(set(waits))}, allowed {sorted(allowed)}")
+        run = 0
+        for i in ins + ["vmcnt(0)"]:
+            if "vmcnt(" in i:
+                if run % lps:
+                    problems.append(f"{name}: {run} loads between waits, stages of {lps}")
+                run = 0
+            elif vmem.match(i):
+                run += 1
+    return problems
+
+
+def test_w8a8_loop_waits_match_its_loads(tmp_path):
+    """The W8A8 GEMM waits for its LDS stages with hand-written vmcnt counts,
+    right only while each stage is exactly kLoadsPerStage vector-memory
+    instructions per thread and nothing else in the K loop uses vector memory
+    (a spill or an extra load would let a stage be read before it lands).
+    Checked on the compiled gfx950 assembly of both instantiations, with
+    planted changes to that assembly as controls."""
+    from quantized_moe_expert_top_amd import build
+    try:
+        build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    lps, stages = _w8a8_geometry()
+    asm = tmp_path / "w8a8.s"
+    r = subprocess.run([build.hipcc(), *build.FLAGS, "--cuda-device-only", "-S", "-o", str(asm),
+                        os.path.join(build.CSRC, "w8a8.hip")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = asm.read_text().splitlines()
+    assert _w8a8_loop_problems(lines, lps, stages) == []
+    # controls: each planted change is caught
+    in_loop, first_dma = False, None
+    for i, l in enumerate(lines):
+        t = l.strip()
+        if t.startswith((".LBB", "; %bb.")):
+            in_loop = "Loop" in t
+        elif in_loop and t.endswith(" lds"):
+            first_dma = i
+            break
+    assert first_dma is not None
+    planted = [
+        [l.replace(f"vmcnt({lps * (stages - 2)})", f"vmcnt({lps * (stages - 2) + 1})") for l in lines],
+        lines[:first_dma] + ["\tglobal_load_dword v1, v[2:3], off"] + lines[first_dma:],
+        lines[:first_dma] + lines[first_dma + 1:],
+        lines[:first_dma] + ["\tscratch_store_dword off, v1, s0"] + lines[first_dma:],
+    ]
+    for bad in planted:
+        assert _w8a8_loop_problems(bad, lps, stages) != []
+
+
 def test_dynamic_lds_arrays_are_16_byte_aligned():
     """A kernel's dynamic LDS starts where its static LDS ends, aligned only to
     the declared alignment of the extern array. The GEMV and GEMM kernels read
